@@ -1,0 +1,275 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged-attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+One step = one decode step of the 8K-context workload: the fused
+slot-mapping KV-cache write of the new token (position 8192) followed by the
+split-K decode over its 8193 keys (page 832, 24 query / 4 KV heads, head 256,
+bf16).  `value` is decode K/V bytes moved per second over the whole timed
+region (K/V bytes = seq_len * 4 heads * 256 * 2 B * 2 for K and V); each step
+reads a different replica of the KV pool so that the reads come from HBM,
+not from the 256 MB Infinity Cache.  The same run also measures the other
+figures the metric names (decode at 32K context for pages 784/832/1024, the
+16-sequence batch, and the q=4096 / q=1685 prefill chunks in TFLOP/s), which
+are reported under "extra".  Prints one JSON line.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor spec
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor spec
+MALL_DEFEAT_BYTES = 2 << 30    # rotate pool replicas over at least this many bytes
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-extra", action="store_true", help="headline workload only")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def kv_bytes(seq_lens, num_kv_heads=4):
+    return int(sum(int(x) for x in seq_lens)) * num_kv_heads * 256 * 2 * 2
+
+
+def causal_flops(start, q_len, num_q_heads=24, head_dim=256):
+    pairs = q_len * start + q_len * (q_len + 1) // 2
+    return 4 * head_dim * num_q_heads * pairs
+
+
+class Dev:
+    def __init__(self):
+        import numpy as np
+        import torch
+        self.np, self.torch = np, torch
+        self.dev = torch.device("cuda:0")
+
+    def t(self, a):
+        a = self.np.ascontiguousarray(a)
+        if a.dtype == self.np.uint16:
+            return self.torch.from_numpy(a.view(self.np.int16)).to(self.dev).view(self.torch.bfloat16)
+        return self.torch.from_numpy(a).to(self.dev)
+
+
+def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False):
+    """Timed decode steps (KV write of the new token + decode); returns a dict."""
+    torch = D.torch
+    k0, v0 = D.t(case.k_cache), D.t(case.v_cache)
+    pool_bytes = 2 * k0.numel() * 2
+    reps = max(1, math.ceil(MALL_DEFEAT_BYTES / pool_bytes)) if rotate else 1
+    ks, vs = [k0], [v0]
+    for _ in range(reps - 1):
+        ks.append(k0.clone())
+        vs.append(v0.clone())
+    bt, sl = D.t(case.block_tables), D.t(case.seq_lens)
+    q = D.t(case.q)
+    has_write = len(case.positions) > 0
+    if has_write:
+        kn, vn = D.t(case.k_new), D.t(case.v_new)
+        pos, seq = D.t(case.positions), D.t(case.token_seq)
+    ws = pa.decode_workspace(q.shape[0], case.max_seq_len, case.block_size, device=D.dev)
+    out = torch.empty_like(q)
+
+    def step(i):
+        r = i % reps
+        if has_write:
+            pa.kv_write_fused(ks[r], vs[r], kn, vn, pos, bt, seq)
+        pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    res = {"replicas": reps}
+    nbytes = kv_bytes(case.seq_lens)
+    if graph:
+        # one graph holds one step per replica; replayed steps // reps times
+        g = torch.cuda.CUDAGraph()
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(reps):
+                    step(i)
+        torch.cuda.current_stream().wait_stream(s)
+        n_rep = max(1, steps // reps)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(n_rep):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / (n_rep * reps)
+        res.update(ms_per_step=ms, gbs=nbytes / (ms * 1e-3) / 1e9)
+        return res
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for i in range(steps):
+        r = i % reps
+        if has_write:
+            pa.kv_write_fused(ks[r], vs[r], kn, vn, pos, bt, seq)
+        evs[i][0].record()
+        pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+        evs[i][1].record()
+    e1.record()
+    torch.cuda.synchronize()
+    total_ms = e0.elapsed_time(e1)
+    kern = sorted(a.elapsed_time(b) for a, b in evs)
+    avg_kernel_ms = sum(kern) / len(kern)
+    res.update(ms_per_step=total_ms / steps, kernel_ms_avg=avg_kernel_ms,
+               kernel_ms_p10=kern[len(kern) // 10], kernel_ms_p50=kern[len(kern) // 2],
+               kernel_ms_p90=kern[(9 * len(kern)) // 10],
+               kv_bytes=nbytes, gbs=nbytes / (total_ms / steps * 1e-3) / 1e9,
+               kernel_gbs=nbytes / (avg_kernel_ms * 1e-3) / 1e9)
+    return res
+
+
+def bench_prefill(D, pa, case, steps, warmup):
+    """Per chunk: the chunk's KV write, then timed attention steps."""
+    torch = D.torch
+    np = D.np
+    k, v = D.t(case.k_cache), D.t(case.v_cache)
+    bt = D.t(case.block_table)
+    out = {}
+    for ch in case.chunks:
+        pos = D.t(np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64))
+        kn, vn, q = D.t(ch.k_new), D.t(ch.v_new), D.t(ch.q)
+        o = torch.empty_like(q)
+        torch.cuda.synchronize()
+        w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        w0.record()
+        pa.kv_write_fused(k, v, kn, vn, pos, bt)
+        w1.record()
+        for _ in range(warmup):
+            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
+        torch.cuda.synchronize()
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)]
+        for i in range(steps):
+            evs[i][0].record()
+            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
+            evs[i][1].record()
+        torch.cuda.synchronize()
+        t = sorted(a.elapsed_time(b) for a, b in evs)
+        avg = sum(t) / len(t)
+        fl = causal_flops(ch.start_pos, ch.q_len)
+        out[f"q{ch.q_len}_start{ch.start_pos}"] = {
+            "kernel_ms_avg": avg, "kernel_ms_p10": t[len(t) // 10], "kernel_ms_p50": t[len(t) // 2],
+            "kernel_ms_p90": t[(9 * len(t)) // 10], "causal_flops": fl,
+            "tflops": fl / (avg * 1e-3) / 1e12, "frac_bf16_peak": fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "kv_write_ms": w0.elapsed_time(w1), "kv_write_bytes": ch.q_len * 4 * 256 * 2 * 2}
+    return out
+
+
+def cpu_baseline(case, seconds):
+    """The fp64 oracle on the headline workload, repeated for ~`seconds`."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count()
+    slots = oracle.slot_mapping(case.positions, case.token_seq, case.block_tables, case.block_size)
+    n, t0 = 0, time.perf_counter()
+    while True:
+        k, v = oracle.kv_write(case.k_cache, case.v_cache, case.k_new, case.v_new, slots)
+        oracle.decode(case.q, k, v, case.block_tables, case.seq_lens, case.block_size, case.scale)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or n >= 1000:
+            break
+    nbytes = kv_bytes(case.seq_lens) * n
+    return {"value": nbytes / el / 1e9, "unit": "GB/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} full decode steps (KV write + decode) of the 8K-context workload, "
+                      f"{el:.1f} s on the host CPU (fp64 NumPy oracle)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(multi-GPU sharding is not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import prefill_block_table_amd as pa
+    import workloads as W
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    D = Dev()
+    print(f"[bench] {pa.build_info()}", file=sys.stderr, flush=True)
+
+    head_case = W.decode_8k()
+    print("[bench] decode_ctx8192_b832 rotated", file=sys.stderr, flush=True)
+    head = bench_decode(D, pa, head_case, args.steps, args.warmup, rotate=True)
+    extra = {"decode_ctx8192_b832": head}
+    if not args.no_extra:
+        print("[bench] decode_ctx8192_b832 warm / graph", file=sys.stderr, flush=True)
+        extra["decode_ctx8192_b832_warm"] = bench_decode(D, pa, head_case, args.steps, args.warmup,
+                                                         rotate=False)
+        extra["decode_ctx8192_b832_graph"] = bench_decode(D, pa, head_case, args.steps,
+                                                          args.warmup, rotate=True, graph=True)
+        for B in (784, 832, 1024):
+            print(f"[bench] decode_ctx32768_b{B}", file=sys.stderr, flush=True)
+            extra[f"decode_ctx32768_b{B}"] = bench_decode(D, pa, W.decode_32k(B), args.steps,
+                                                          args.warmup, rotate=True)
+        print("[bench] decode_batch16", file=sys.stderr, flush=True)
+        extra["decode_batch16_ctx4k_32k_b832"] = bench_decode(D, pa, W.batched_decode(),
+                                                              max(20, args.steps // 4),
+                                                              args.warmup, rotate=True)
+        print("[bench] prefill", file=sys.stderr, flush=True)
+        extra["prefill_b832"] = bench_prefill(D, pa, W.prefill_8k(), max(10, args.steps // 5),
+                                              min(args.warmup, 5))
+    torch.cuda.synchronize()
+
+    cpu = None
+    if not args.no_cpu:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(head_case, args.cpu_seconds)
+
+    achieved = head["kernel_gbs"]
+    line = {
+        "metric": "decode K/V GB/s (% HBM peak) @8K/32K ctx; prefill q=4096 TFLOP/s (% MFMA)",
+        "value": round(head["gbs"], 3),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(head["ms_per_step"], 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) bf16 K/V/q, random block tables)",
+        "config": {"workload": "decode_ctx8192_b832: 1 seq, 8192 cached tokens + 1 written at "
+                               "position 8192 (slot-mapping KV write + split-K decode), page 832, "
+                               "pool 64 pages, 24 q / 4 KV heads, head_dim 256",
+                   "kv_bytes_per_step": head["kv_bytes"], "pool_replicas": head["replicas"]},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel", "kernel_ms_avg": head["kernel_ms_avg"]},
+        "cpu_baseline": cpu,
+        "extra": extra,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,196 @@
+/*
+ * pa.h - paged-KV grouped-query attention for AMD MI355X (gfx950).
+ *
+ * C ABI of libpa.so.  Plain pointers and sizes only.
+ *
+ * Sources (the pages this library implements):
+ *  [ALIGN] luanjiahao.me, post on aligning the Qwen3.5 KV page from 784 to
+ *          832 tokens for DCU paged attention.
+ *  [PREP]  jsqmd.com/news/1214744, "2026 先导杯实战：别只盯着大算子，把
+ *          Qwen3.5 vLLM 单 Token 输入准备搬上 DCU" (single-token decode
+ *          input preparation).
+ *
+ * Conventions shared by every call
+ *  - Every pointer argument is a DEVICE pointer (memory the caller allocated
+ *    with hipMalloc or a framework on top of it), except the size_t* outputs
+ *    of pa_decode_workspace_size, which are host pointers.
+ *  - bf16 tensors are passed as uint16_t* holding bf16 bit patterns.  All
+ *    bf16 tensors must be 16-byte aligned.
+ *  - KV cache layout ([ALIGN] §4): K and V are separate tensors, each
+ *    [num_pages][block_size][num_kv_heads][head_dim] with rows of
+ *    num_kv_heads*head_dim contiguous elements; consecutive pages are
+ *    page_stride ELEMENTS apart (page_stride >= block_size*num_kv_heads*
+ *    head_dim), so the joint [num_pages][2][block_size][..] layout of the
+ *    pages works with k_cache = base, v_cache = base + block_size*Hkv*D and
+ *    page_stride = 2*block_size*Hkv*D.
+ *  - Block tables are int32 [num_seqs][bt_stride] row-major; entry p of row s
+ *    is the physical page of logical page p ([ALIGN] §1: logical_page =
+ *    t / block_size, page_offset = t % block_size, physical_page =
+ *    block_table[logical_page]).
+ *  - Supported shapes: head_dim == 256, num_q_heads == 6 * num_kv_heads
+ *    (GQA ratio 6, [ALIGN] §4), 1 <= num_kv_heads <= 64.  Others return
+ *    PA_ERR_UNSUPPORTED.  Any block_size >= 1 works; pages whose size is not
+ *    a multiple of 64 cost one masked tail group per page.
+ *  - Ownership: the caller owns every buffer, including the decode
+ *    workspace.  The library never allocates or frees device memory and
+ *    keeps no state between calls (the workspace's counters are left at zero
+ *    by each completed call).
+ *  - Execution: each call validates its arguments on the host, then only
+ *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
+ *    returns without synchronizing.  On any error nothing is enqueued.
+ *  - Errors: 0 on success, a negative PA_ERR_* code otherwise; nothing is
+ *    thrown or aborted across the ABI.  pa_strerror() names a code.
+ *  - Device-side preconditions (not checkable on the host, not checked in
+ *    kernels): block-table entries that a call reads (logical pages below
+ *    ceil(len / block_size)) lie in [0, num_pages); entries past that are
+ *    never read.
+ */
+#ifndef PA_H_
+#define PA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PA_OK 0
+#define PA_ERR_NULL -1          /* a required pointer is NULL */
+#define PA_ERR_BLOCK_SIZE -2    /* block_size < 1 */
+#define PA_ERR_UNSUPPORTED -3   /* head_dim / head counts outside the supported set */
+#define PA_ERR_SIZE -4          /* a count or position is out of range */
+#define PA_ERR_WORKSPACE -5     /* decode workspace NULL or too small */
+#define PA_ERR_TABLE -6         /* lengths need more block-table entries than given */
+#define PA_ERR_STRIDE -7        /* page_stride smaller than one page */
+#define PA_ERR_ALIGN -8         /* a bf16 tensor is not 16-byte aligned */
+#define PA_ERR_LAUNCH -9        /* the HIP runtime rejected a kernel launch */
+
+/*
+ * Slot mapping ([PREP] §3.2 and §5): for each token i,
+ *   slot[i] = block_table[seq][pos / block_size] * block_size + pos % block_size
+ * with pos = positions[i] and seq = token_seq[i] (token_seq NULL => seq 0).
+ *
+ * slot_out   int64 [num_tokens], written.
+ * positions  int64 [num_tokens].  A negative position, or one whose logical
+ *            page is >= bt_stride, yields slot -1 (no table read).
+ * token_seq  int32 [num_tokens] or NULL.
+ * block_table int32 [*][bt_stride].
+ * num_tokens >= 0 (0 enqueues nothing).
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_SIZE (num_tokens < 0 or
+ * bt_stride < 1), PA_ERR_LAUNCH.
+ */
+int pa_slot_mapping(int64_t* slot_out, const int64_t* positions, const int32_t* token_seq,
+                    int32_t num_tokens, const int32_t* block_table, int32_t bt_stride,
+                    int32_t block_size, void* stream);
+
+/*
+ * KV-cache write through a slot mapping ([PREP] §2-§3: the KV-cache write
+ * position of each new token is its slot): copies k_new[i] (num_kv_heads *
+ * head_dim bf16) to row slot % block_size of page slot / block_size of
+ * k_cache, and v_new[i] likewise to v_cache.  Bit copy, no arithmetic.
+ * Slots outside [0, num_pages * block_size) (e.g. -1 padding) are skipped.
+ * Two tokens with the same slot: which one lands is unspecified.
+ *
+ * k_cache, v_cache  bf16 caches (layout above), modified in place.
+ * k_new, v_new      bf16 [num_tokens][num_kv_heads][head_dim].
+ * slot_mapping      int64 [num_tokens].
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE
+ * (num_tokens < 0, num_pages < 1), PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_LAUNCH.
+ */
+int pa_kv_write(uint16_t* k_cache, uint16_t* v_cache, int64_t page_stride, int32_t num_pages,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                const uint16_t* k_new, const uint16_t* v_new, int32_t num_tokens,
+                const int64_t* slot_mapping, void* stream);
+
+/*
+ * Fused slot mapping + KV-cache write: one launch computes each token's slot
+ * from positions / token_seq / block_table exactly as pa_slot_mapping does,
+ * optionally stores it to slot_out (NULL = do not store), and writes the
+ * token's K/V rows as pa_kv_write does.  Same errors as both.
+ */
+int pa_kv_write_fused(uint16_t* k_cache, uint16_t* v_cache, int64_t page_stride,
+                      int32_t num_pages, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_dim, const uint16_t* k_new, const uint16_t* v_new,
+                      int32_t num_tokens, const int64_t* positions, const int32_t* token_seq,
+                      const int32_t* block_table, int32_t bt_stride, int64_t* slot_out,
+                      void* stream);
+
+/*
+ * Bytes of device workspace pa_decode needs for this batch shape.  The
+ * workspace holds split-K partial results and one arrival counter per
+ * (sequence, KV head).  It must be zero-filled once before its first use;
+ * every completed pa_decode call leaves its counters at zero again, so it
+ * can be reused by later calls of the same or smaller shape on the same
+ * stream.  Two pa_decode calls that share a workspace must not overlap.
+ * bytes_out: host pointer.
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE.
+ */
+int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
+                             int32_t num_kv_heads, size_t* bytes_out);
+
+/*
+ * Single-token (q = 1) paged GQA decode ([ALIGN] §7: walk the pages of each
+ * sequence in order, look up block_table once per page, iterate 64-token
+ * groups inside the page, online softmax; no page skipped, causal range not
+ * shortened).  For each sequence s and query head h (KV head g = h / 6):
+ *   out[s][h] = sum_j softmax_j(scale * q[s][h] . K_j) * V_j
+ * over the seq_lens[s] keys j = 0 .. seq_lens[s]-1 of sequence s; the query
+ * is the token at position seq_lens[s]-1, whose K/V must already be in the
+ * cache (seq_lens = position + 1, [PREP] §2).  Computed in fp32 from bf16
+ * inputs, written as bf16 (round to nearest even).
+ *
+ * out           bf16 [num_seqs][num_q_heads][256], written.
+ * q             bf16 [num_seqs][num_q_heads][256].
+ * seq_lens      int32 [num_seqs]; values are clamped to [0, max_seq_len];
+ *               a sequence of length 0 gets an all-zero output.
+ * max_seq_len   host-side bound on seq_lens, >= 1, and
+ *               <= bt_stride * block_size.
+ * workspace     device buffer of >= pa_decode_workspace_size(...) bytes,
+ *               zero-filled before first use (see above).
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE
+ * (num_seqs < 1, max_seq_len < 1), PA_ERR_TABLE, PA_ERR_STRIDE,
+ * PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_LAUNCH.
+ */
+int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+              const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
+              int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+              int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, void* workspace,
+              size_t workspace_bytes, void* stream);
+
+/*
+ * Attention for one chunk of a chunked prefill of a single sequence
+ * ([ALIGN] §6: q_len query tokens at positions start_pos .. start_pos +
+ * q_len - 1, with the paged KV of the first start_pos + q_len tokens,
+ * complete causal attention).  The chunk's own K/V must already be in the
+ * cache.  For chunk row i and query head h (KV head g = h / 6):
+ *   out[i][h] = sum_j softmax_j(scale * q_chunk[i][h] . K_j) * V_j
+ * over keys j <= start_pos + i when causal != 0, over all start_pos + q_len
+ * keys when causal == 0.  bf16 MFMA products with fp32 accumulation; the
+ * softmax weights are rounded to bf16 before the PV product; output bf16.
+ *
+ * out, q_chunk   bf16 [q_len][num_q_heads][256].
+ * block_table    int32 [num_table_entries] (one sequence's row);
+ *                ceil((start_pos + q_len) / block_size) <= num_table_entries.
+ * q_len >= 1, start_pos >= 0, start_pos + q_len < 2^31.
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE,
+ * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_LAUNCH.
+ */
+int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int32_t start_pos,
+                     int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
+                     int64_t page_stride, const int32_t* block_table, int32_t num_table_entries,
+                     int32_t block_size, float scale, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, void* stream);
+
+/* Static string naming an error code (never NULL). */
+const char* pa_strerror(int code);
+
+/* Static string: library version, gfx target and kernel variant ids. */
+const char* pa_build_info(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PA_H_ */

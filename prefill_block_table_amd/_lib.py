@@ -1,0 +1,216 @@
+"""ctypes loader and argument marshalling for libpa.so (see include/pa.h)."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libpa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build the HIP library first with "
+        "`python -m prefill_block_table_amd.build` (or __graft_entry__.build())")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+_i32, _i64, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+lib.pa_slot_mapping.argtypes = [_vp, _vp, _vp, _i32, _vp, _i32, _i32, _vp]
+lib.pa_kv_write.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32, _vp, _vp]
+lib.pa_kv_write_fused.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _vp, _i32,
+                                  _vp, _vp, _vp, _i32, _vp, _vp]
+lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
+lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                          _i32, _i32, _i32, _vp, _sz, _vp]
+lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
+                                 _f32, _i32, _i32, _i32, _vp]
+for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
+           "pa_decode", "pa_prefill_chunk"):
+    getattr(lib, _f).restype = ctypes.c_int
+lib.pa_strerror.argtypes = [ctypes.c_int]
+lib.pa_strerror.restype = ctypes.c_char_p
+lib.pa_build_info.argtypes = []
+lib.pa_build_info.restype = ctypes.c_char_p
+
+HEAD_DIM = 256
+GQA = 6
+
+
+class PAError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        self.code = code
+        super().__init__(f"{where}: {strerror(code)} (code {code})")
+
+
+def strerror(code: int) -> str:
+    return lib.pa_strerror(int(code)).decode()
+
+
+def build_info() -> str:
+    return lib.pa_build_info().decode()
+
+
+def _check(rc: int, where: str) -> None:
+    if rc != 0:
+        raise PAError(rc, where)
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t: torch.Tensor, name: str, dtypes, device=None, contiguous=True):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if contiguous and not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+
+
+def _cache_geometry(k_cache: torch.Tensor, v_cache: torch.Tensor):
+    """(num_pages, block_size, num_kv_heads, page_stride) of [P, B, Hkv, 256] caches.
+
+    Pages may be strided (e.g. K and V views of a joint [P, 2, B, Hkv, D]
+    tensor); rows inside a page must be contiguous.
+    """
+    for t, n in ((k_cache, "k_cache"), (v_cache, "v_cache")):
+        _need(t, n, _BF16, contiguous=False)
+        if t.dim() != 4 or t.shape[3] != HEAD_DIM:
+            raise ValueError(f"{n} must be [num_pages, block_size, num_kv_heads, 256]")
+        P, B, H, D = t.shape
+        if t.stride(3) != 1 or t.stride(2) != D or t.stride(1) != H * D:
+            raise ValueError(f"{n}: rows inside a page must be contiguous")
+    if k_cache.shape != v_cache.shape or k_cache.stride(0) != v_cache.stride(0):
+        raise ValueError("k_cache and v_cache must have the same shape and page stride")
+    P, B, H, _ = k_cache.shape
+    return P, B, H, k_cache.stride(0)
+
+
+def slot_mapping(positions: torch.Tensor, block_table: torch.Tensor, block_size: int,
+                 token_seq: torch.Tensor = None, out: torch.Tensor = None) -> torch.Tensor:
+    """slot[i] = block_table[seq_i][pos_i // B] * B + pos_i % B (int64)."""
+    _need(positions, "positions", (torch.int64,))
+    _need(block_table, "block_table", (torch.int32,), positions.device)
+    if token_seq is not None:
+        _need(token_seq, "token_seq", (torch.int32,), positions.device)
+    bt = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    if out is None:
+        out = torch.empty_like(positions)
+    _need(out, "out", (torch.int64,), positions.device)
+    _check(lib.pa_slot_mapping(_ptr(out), _ptr(positions), _ptr(token_seq), positions.numel(),
+                               _ptr(bt), bt.shape[1], int(block_size), _stream(positions)),
+           "pa_slot_mapping")
+    return out
+
+
+def kv_write(k_cache, v_cache, k_new, v_new, slot_mapping: torch.Tensor) -> None:
+    """Scatter k_new/v_new [T, Hkv, 256] to the cache rows named by slot_mapping."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(k_new, "k_new", _BF16, k_cache.device)
+    _need(v_new, "v_new", _BF16, k_cache.device)
+    _need(slot_mapping, "slot_mapping", (torch.int64,), k_cache.device)
+    T = slot_mapping.numel()
+    if k_new.shape != (T, H, HEAD_DIM) or v_new.shape != (T, H, HEAD_DIM):
+        raise ValueError("k_new/v_new must be [num_tokens, num_kv_heads, 256]")
+    _check(lib.pa_kv_write(_ptr(k_cache), _ptr(v_cache), stride, P, B, H, HEAD_DIM,
+                           _ptr(k_new), _ptr(v_new), T, _ptr(slot_mapping), _stream(k_cache)),
+           "pa_kv_write")
+
+
+def kv_write_fused(k_cache, v_cache, k_new, v_new, positions: torch.Tensor,
+                   block_table: torch.Tensor, token_seq: torch.Tensor = None,
+                   slot_out: torch.Tensor = None) -> None:
+    """Slot mapping and KV write in one launch; optionally stores the slots."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(k_new, "k_new", _BF16, k_cache.device)
+    _need(v_new, "v_new", _BF16, k_cache.device)
+    _need(positions, "positions", (torch.int64,), k_cache.device)
+    _need(block_table, "block_table", (torch.int32,), k_cache.device)
+    if token_seq is not None:
+        _need(token_seq, "token_seq", (torch.int32,), k_cache.device)
+    if slot_out is not None:
+        _need(slot_out, "slot_out", (torch.int64,), k_cache.device)
+    bt = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    T = positions.numel()
+    if k_new.shape != (T, H, HEAD_DIM) or v_new.shape != (T, H, HEAD_DIM):
+        raise ValueError("k_new/v_new must be [num_tokens, num_kv_heads, 256]")
+    _check(lib.pa_kv_write_fused(_ptr(k_cache), _ptr(v_cache), stride, P, B, H, HEAD_DIM,
+                                 _ptr(k_new), _ptr(v_new), T, _ptr(positions), _ptr(token_seq),
+                                 _ptr(bt), bt.shape[1], _ptr(slot_out), _stream(k_cache)),
+           "pa_kv_write_fused")
+
+
+def decode_workspace_size(num_seqs: int, max_seq_len: int, block_size: int,
+                          num_kv_heads: int = 4) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.pa_decode_workspace_size(int(num_seqs), int(max_seq_len), int(block_size),
+                                        int(num_kv_heads), ctypes.byref(n)),
+           "pa_decode_workspace_size")
+    return n.value
+
+
+def decode_workspace(num_seqs: int, max_seq_len: int, block_size: int, num_kv_heads: int = 4,
+                     device="cuda") -> torch.Tensor:
+    """A zero-filled workspace of the size pa_decode needs (reusable)."""
+    return torch.zeros(decode_workspace_size(num_seqs, max_seq_len, block_size, num_kv_heads),
+                       dtype=torch.uint8, device=device)
+
+
+def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale: float,
+           workspace: torch.Tensor = None, out: torch.Tensor = None) -> torch.Tensor:
+    """q [S, 6*Hkv, 256] -> out [S, 6*Hkv, 256] bf16 (one query per sequence)."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(q, "q", _BF16, k_cache.device)
+    _need(block_table, "block_table", (torch.int32,), k_cache.device)
+    _need(seq_lens, "seq_lens", (torch.int32,), k_cache.device)
+    S = q.shape[0]
+    if q.shape != (S, GQA * H, HEAD_DIM):
+        raise ValueError("q must be [num_seqs, 6 * num_kv_heads, 256]")
+    bt = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    if bt.shape[0] < S or seq_lens.numel() < S:
+        raise ValueError("block_table / seq_lens have fewer rows than q")
+    if workspace is None:
+        workspace = decode_workspace(S, max_seq_len, B, H, device=q.device)
+    _need(workspace, "workspace", (torch.uint8,), k_cache.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, k_cache.device)
+    _check(lib.pa_decode(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), stride, _ptr(bt),
+                         bt.shape[1], _ptr(seq_lens), S, int(max_seq_len), B, float(scale),
+                         GQA * H, H, HEAD_DIM, _ptr(workspace), workspace.numel(), _stream(q)),
+           "pa_decode")
+    return out
+
+
+def prefill_chunk(q_chunk, k_cache, v_cache, block_table, start_pos: int, scale: float,
+                  causal: bool = True, out: torch.Tensor = None) -> torch.Tensor:
+    """q_chunk [q_len, 6*Hkv, 256] at positions start_pos.. -> out, same shape (bf16)."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(q_chunk, "q_chunk", _BF16, k_cache.device)
+    _need(block_table, "block_table", (torch.int32,), k_cache.device)
+    q_len = q_chunk.shape[0]
+    if q_chunk.shape != (q_len, GQA * H, HEAD_DIM):
+        raise ValueError("q_chunk must be [q_len, 6 * num_kv_heads, 256]")
+    bt = block_table.reshape(-1)
+    if out is None:
+        out = torch.empty_like(q_chunk)
+    _need(out, "out", _BF16, k_cache.device)
+    _check(lib.pa_prefill_chunk(_ptr(out), _ptr(q_chunk), q_len, int(start_pos), int(bool(causal)),
+                                _ptr(k_cache), _ptr(v_cache), stride, _ptr(bt), bt.numel(), B,
+                                float(scale), GQA * H, H, HEAD_DIM, _stream(q_chunk)),
+           "pa_prefill_chunk")
+    return out

@@ -1,0 +1,184 @@
+// C ABI of libpa: argument validation, plan sizing and kernel launches.
+// Every check happens on the host before anything is enqueued.
+#include "../../include/pa.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <string>
+
+#include "pa_internal.h"
+
+#ifndef PA_GIT_REV
+#define PA_GIT_REV "unknown"
+#endif
+
+namespace {
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_heads(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  if (head_dim != pa::kHeadDimAbi) return PA_ERR_UNSUPPORTED;
+  if (num_kv_heads < 1 || num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
+  if (num_q_heads != 6 * num_kv_heads) return PA_ERR_UNSUPPORTED;
+  return PA_OK;
+}
+
+int check_cache(const uint16_t* k_cache, const uint16_t* v_cache, int64_t page_stride,
+                int32_t block_size, int32_t num_kv_heads) {
+  if (!k_cache || !v_cache) return PA_ERR_NULL;
+  if (block_size < 1) return PA_ERR_BLOCK_SIZE;
+  if (page_stride < (int64_t)block_size * num_kv_heads * pa::kHeadDimAbi) return PA_ERR_STRIDE;
+  if (page_stride % 8 != 0) return PA_ERR_ALIGN;
+  if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? PA_OK : PA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+int pa_slot_mapping(int64_t* slot_out, const int64_t* positions, const int32_t* token_seq,
+                    int32_t num_tokens, const int32_t* block_table, int32_t bt_stride,
+                    int32_t block_size, void* stream) {
+  if (!slot_out || !positions || !block_table) return PA_ERR_NULL;
+  if (block_size < 1) return PA_ERR_BLOCK_SIZE;
+  if (num_tokens < 0 || bt_stride < 1) return PA_ERR_SIZE;
+  if (num_tokens == 0) return PA_OK;
+  return launch_status(pa::launch_slot_mapping(slot_out, positions, token_seq, num_tokens,
+                                               block_table, bt_stride, block_size,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+static int kv_write_common(uint16_t* k_cache, uint16_t* v_cache, int64_t page_stride,
+                           int32_t num_pages, int32_t block_size, int32_t num_kv_heads,
+                           int32_t head_dim, const uint16_t* k_new, const uint16_t* v_new,
+                           int32_t num_tokens) {
+  if (!k_new || !v_new) return PA_ERR_NULL;
+  int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
+  if (rc) return rc;
+  if (head_dim != pa::kHeadDimAbi || num_kv_heads < 1 || num_kv_heads > 64)
+    return PA_ERR_UNSUPPORTED;
+  if (num_tokens < 0 || num_pages < 1) return PA_ERR_SIZE;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_ALIGN;
+  return PA_OK;
+}
+
+int pa_kv_write(uint16_t* k_cache, uint16_t* v_cache, int64_t page_stride, int32_t num_pages,
+                int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                const uint16_t* k_new, const uint16_t* v_new, int32_t num_tokens,
+                const int64_t* slot_mapping, void* stream) {
+  if (!slot_mapping) return PA_ERR_NULL;
+  int rc = kv_write_common(k_cache, v_cache, page_stride, num_pages, block_size, num_kv_heads,
+                           head_dim, k_new, v_new, num_tokens);
+  if (rc) return rc;
+  if (num_tokens == 0) return PA_OK;
+  return launch_status(pa::launch_kv_write(k_cache, v_cache, page_stride, num_pages, block_size,
+                                           num_kv_heads, k_new, v_new, num_tokens, slot_mapping,
+                                           nullptr, nullptr, nullptr, 0, nullptr,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+int pa_kv_write_fused(uint16_t* k_cache, uint16_t* v_cache, int64_t page_stride,
+                      int32_t num_pages, int32_t block_size, int32_t num_kv_heads,
+                      int32_t head_dim, const uint16_t* k_new, const uint16_t* v_new,
+                      int32_t num_tokens, const int64_t* positions, const int32_t* token_seq,
+                      const int32_t* block_table, int32_t bt_stride, int64_t* slot_out,
+                      void* stream) {
+  if (!positions || !block_table) return PA_ERR_NULL;
+  int rc = kv_write_common(k_cache, v_cache, page_stride, num_pages, block_size, num_kv_heads,
+                           head_dim, k_new, v_new, num_tokens);
+  if (rc) return rc;
+  if (bt_stride < 1) return PA_ERR_SIZE;
+  if (num_tokens == 0) return PA_OK;
+  return launch_status(pa::launch_kv_write(k_cache, v_cache, page_stride, num_pages, block_size,
+                                           num_kv_heads, k_new, v_new, num_tokens, nullptr,
+                                           positions, token_seq, block_table, bt_stride,
+                                           slot_out, static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
+                             int32_t num_kv_heads, size_t* bytes_out) {
+  if (!bytes_out) return PA_ERR_NULL;
+  if (block_size < 1) return PA_ERR_BLOCK_SIZE;
+  if (num_kv_heads < 1 || num_kv_heads > 64) return PA_ERR_UNSUPPORTED;
+  if (num_seqs < 1 || num_seqs > 65535 || max_seq_len < 1 ||
+      (int64_t)max_seq_len + block_size > INT32_MAX)
+    return PA_ERR_SIZE;
+  *bytes_out = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads).bytes;
+  return PA_OK;
+}
+
+int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+              const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
+              int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+              int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  if (!out || !q || !block_table || !seq_lens) return PA_ERR_NULL;
+  int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  if (num_seqs < 1 || num_seqs > 65535 || max_seq_len < 1 ||
+      (int64_t)max_seq_len + block_size > INT32_MAX)
+    return PA_ERR_SIZE;
+  if (bt_stride < 1 || (int64_t)bt_stride * block_size < max_seq_len) return PA_ERR_TABLE;
+  if (!aligned16(out) || !aligned16(q)) return PA_ERR_ALIGN;
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads);
+  if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+  return launch_status(pa::launch_decode(out, q, k_cache, v_cache, page_stride, block_table,
+                                         bt_stride, seq_lens, num_seqs, max_seq_len, block_size,
+                                         scale, num_kv_heads, plan, workspace,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int32_t start_pos,
+                     int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
+                     int64_t page_stride, const int32_t* block_table, int32_t num_table_entries,
+                     int32_t block_size, float scale, int32_t num_q_heads, int32_t num_kv_heads,
+                     int32_t head_dim, void* stream) {
+  if (!out || !q_chunk || !block_table) return PA_ERR_NULL;
+  int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  if (q_len < 1 || start_pos < 0 || (int64_t)start_pos + q_len + block_size > INT32_MAX)
+    return PA_ERR_SIZE;
+  const int64_t kv_len = (int64_t)start_pos + q_len;
+  if (num_table_entries < 1 || (int64_t)num_table_entries * block_size < kv_len)
+    return PA_ERR_TABLE;
+  if (!aligned16(out) || !aligned16(q_chunk)) return PA_ERR_ALIGN;
+  return launch_status(pa::launch_prefill(out, q_chunk, q_len, start_pos, causal, k_cache,
+                                          v_cache, page_stride, block_table, block_size, scale,
+                                          num_kv_heads, static_cast<hipStream_t>(stream)));
+}
+
+const char* pa_strerror(int code) {
+  switch (code) {
+    case PA_OK: return "ok";
+    case PA_ERR_NULL: return "a required pointer is NULL";
+    case PA_ERR_BLOCK_SIZE: return "block_size must be >= 1";
+    case PA_ERR_UNSUPPORTED: return "unsupported shape: need head_dim 256, num_q_heads = 6 * num_kv_heads, 1 <= num_kv_heads <= 64";
+    case PA_ERR_SIZE: return "a count or position is out of range";
+    case PA_ERR_WORKSPACE: return "decode workspace is NULL or smaller than pa_decode_workspace_size()";
+    case PA_ERR_TABLE: return "the block table has fewer entries than the lengths need";
+    case PA_ERR_STRIDE: return "page_stride is smaller than one page";
+    case PA_ERR_ALIGN: return "a tensor is not aligned (bf16 tensors: 16 bytes, workspace: 256 bytes)";
+    case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    default: return "unknown error code";
+  }
+}
+
+const char* pa_build_info(void) {
+  static const std::string info = std::string("libpa rev=") + PA_GIT_REV +
+                                 " target=gfx950 " + pa::kDecodeVariant + " " +
+                                 pa::kPrefillVariant + " kv_write-v1(one-wg-per-token)";
+  return info.c_str();
+}
+
+}  // extern "C"

@@ -1,0 +1,135 @@
+"""C-ABI library: loads, exports what include/pa.h declares, rejects bad
+arguments on the host before touching a device (CPU only, no kernel runs)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "pa.h")
+
+pa = pytest.importorskip("prefill_block_table_amd")
+
+P = ctypes.c_void_p
+FAKE = ctypes.c_void_p(0x10000)       # aligned, never dereferenced: every call below fails validation
+FAKE_MIS = ctypes.c_void_p(0x10002)   # misaligned
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(pa_[a-z_0-9]+)\s*\(", text)))
+
+
+def _codes():
+    text = open(HEADER).read()
+    return {m[0]: int(m[1]) for m in re.findall(r"#define (PA_[A-Z_]+) (-?\d+)", text)}
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == {"pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused",
+                          "pa_decode_workspace_size", "pa_decode", "pa_prefill_chunk",
+                          "pa_strerror", "pa_build_info"}
+    out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
+                         text=True).stdout
+    exported = set(re.findall(r" T (pa_\w+)", out))
+    assert set(names) <= exported
+    for n in names:
+        assert hasattr(pa.lib, n)
+
+
+def test_build_info_and_strerror():
+    info = pa.build_info()
+    assert "gfx950" in info and "decode-" in info and "prefill-" in info
+    for name, code in _codes().items():
+        s = pa.strerror(code)
+        assert s and s != "unknown error code", name
+    assert pa.strerror(12345) == "unknown error code"
+
+
+C = _codes()
+
+
+def _decode(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, page_stride=832 * 1024, bt=FAKE, bt_stride=10,
+                seq_lens=FAKE, num_seqs=1, max_seq_len=8193, B=832, scale=0.0625, hq=24, hkv=4,
+                d=256, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return pa.lib.pa_decode(args["out"], args["q"], args["k"], args["v"], args["page_stride"],
+                            args["bt"], args["bt_stride"], args["seq_lens"], args["num_seqs"],
+                            args["max_seq_len"], args["B"], args["scale"], args["hq"],
+                            args["hkv"], args["d"], args["ws"], args["ws_bytes"], None)
+
+
+def test_decode_validation():
+    assert _decode(out=None) == C["PA_ERR_NULL"]
+    assert _decode(seq_lens=None) == C["PA_ERR_NULL"]
+    assert _decode(B=0) == C["PA_ERR_BLOCK_SIZE"]
+    assert _decode(d=128) == C["PA_ERR_UNSUPPORTED"]
+    assert _decode(hq=32) == C["PA_ERR_UNSUPPORTED"]
+    assert _decode(hkv=0, hq=0) == C["PA_ERR_UNSUPPORTED"]
+    assert _decode(num_seqs=0) == C["PA_ERR_SIZE"]
+    assert _decode(max_seq_len=0) == C["PA_ERR_SIZE"]
+    assert _decode(bt_stride=9) == C["PA_ERR_TABLE"]           # 9 * 832 < 8193
+    assert _decode(page_stride=832 * 1024 - 8) == C["PA_ERR_STRIDE"]
+    assert _decode(q=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    assert _decode(k=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    assert _decode(ws=None) == C["PA_ERR_WORKSPACE"]
+    need = pa.decode_workspace_size(1, 8193, 832, 4)
+    assert _decode(ws_bytes=need - 1) == C["PA_ERR_WORKSPACE"]
+
+
+def test_workspace_size_monotone():
+    a = pa.decode_workspace_size(1, 8193, 832)
+    b = pa.decode_workspace_size(16, 32769, 832)
+    assert 0 < a < b
+    with pytest.raises(pa.PAError):
+        pa.decode_workspace_size(0, 10, 16)
+    with pytest.raises(pa.PAError):
+        pa.decode_workspace_size(1, 10, 0)
+
+
+def _prefill(**kw):
+    args = dict(out=FAKE, q=FAKE, q_len=4096, start=4096, causal=1, k=FAKE, v=FAKE,
+                page_stride=832 * 1024, bt=FAKE, n_bt=10, B=832, scale=0.0625, hq=24, hkv=4,
+                d=256)
+    args.update(kw)
+    return pa.lib.pa_prefill_chunk(args["out"], args["q"], args["q_len"], args["start"],
+                                   args["causal"], args["k"], args["v"], args["page_stride"],
+                                   args["bt"], args["n_bt"], args["B"], args["scale"],
+                                   args["hq"], args["hkv"], args["d"], None)
+
+
+def test_prefill_validation():
+    assert _prefill(q=None) == C["PA_ERR_NULL"]
+    assert _prefill(bt=None) == C["PA_ERR_NULL"]
+    assert _prefill(B=-1) == C["PA_ERR_BLOCK_SIZE"]
+    assert _prefill(d=64) == C["PA_ERR_UNSUPPORTED"]
+    assert _prefill(q_len=0) == C["PA_ERR_SIZE"]
+    assert _prefill(start=-1) == C["PA_ERR_SIZE"]
+    assert _prefill(start=2 ** 31 - 100) == C["PA_ERR_SIZE"]
+    assert _prefill(n_bt=9) == C["PA_ERR_TABLE"]               # 9 * 832 < 8192
+    assert _prefill(page_stride=100) == C["PA_ERR_STRIDE"]
+    assert _prefill(out=FAKE_MIS) == C["PA_ERR_ALIGN"]
+
+
+def test_kv_write_and_slot_mapping_validation():
+    L = pa.lib
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE, FAKE, 1, None, None) == C["PA_ERR_NULL"]
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 64, 832, 4, 128, FAKE, FAKE, 1, FAKE, None) == C["PA_ERR_UNSUPPORTED"]
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 0, 832, 4, 256, FAKE, FAKE, 1, FAKE, None) == C["PA_ERR_SIZE"]
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE, FAKE, -1, FAKE, None) == C["PA_ERR_SIZE"]
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 64, 0, 4, 256, FAKE, FAKE, 1, FAKE, None) == C["PA_ERR_BLOCK_SIZE"]
+    assert L.pa_kv_write(FAKE, FAKE, 1024, 64, 832, 4, 256, FAKE, FAKE, 1, FAKE, None) == C["PA_ERR_STRIDE"]
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE_MIS, FAKE, 1, FAKE, None) == C["PA_ERR_ALIGN"]
+    # zero tokens: valid, nothing enqueued
+    assert L.pa_kv_write(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE, FAKE, 0, FAKE, None) == 0
+    assert L.pa_kv_write_fused(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE, FAKE, 1, None, None, FAKE, 10, None, None) == C["PA_ERR_NULL"]
+    assert L.pa_kv_write_fused(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE, FAKE, 1, FAKE, None, FAKE, 0, None, None) == C["PA_ERR_SIZE"]
+    assert L.pa_kv_write_fused(FAKE, FAKE, 832 * 1024, 64, 832, 4, 256, FAKE, FAKE, 0, FAKE, None, FAKE, 10, None, None) == 0
+    assert L.pa_slot_mapping(None, FAKE, None, 1, FAKE, 10, 832, None) == C["PA_ERR_NULL"]
+    assert L.pa_slot_mapping(FAKE, FAKE, None, 1, FAKE, 10, 0, None) == C["PA_ERR_BLOCK_SIZE"]
+    assert L.pa_slot_mapping(FAKE, FAKE, None, -5, FAKE, 10, 832, None) == C["PA_ERR_SIZE"]
+    assert L.pa_slot_mapping(FAKE, FAKE, None, 0, FAKE, 10, 832, None) == 0
