@@ -64,7 +64,50 @@ class Dev:
         return self.torch.from_numpy(a).to(self.dev)
 
 
-def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False):
+_SLEEP_CYCLES_PER_MS = None
+
+
+def gpu_hold(torch, ms):
+    """Keep the GPU busy for about `ms` so the host can enqueue the timed steps
+    ahead of the device; the timed region then measures device execution, not
+    Python launch overhead.  Not part of any timed region."""
+    global _SLEEP_CYCLES_PER_MS
+    if _SLEEP_CYCLES_PER_MS is None:
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        torch.cuda._sleep(2_000_000)
+        b.record()
+        torch.cuda.synchronize()
+        _SLEEP_CYCLES_PER_MS = 2_000_000 / max(a.elapsed_time(b), 1e-3)
+    torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
+
+
+def timed_loop(torch, steps, launch_step, hold_ms):
+    """Run `steps` steps after a GPU hold; returns (total_ms, per-step kernel
+    ms of the bracketed launch, host enqueue seconds)."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    gpu_hold(torch, hold_ms)
+    t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        launch_step(i, evs[i])
+    e1.record()
+    host_s = time.perf_counter() - t0
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1), [a.elapsed_time(b) for a, b in evs], host_s
+
+
+def _stats(ts):
+    t = sorted(ts)
+    return {"kernel_ms_avg": sum(t) / len(t), "kernel_ms_p10": t[len(t) // 10],
+            "kernel_ms_p50": t[len(t) // 2], "kernel_ms_p90": t[(9 * len(t)) // 10]}
+
+
+def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=None):
     """Timed decode steps (KV write of the new token + decode); returns a dict."""
     torch = D.torch
     k0, v0 = D.t(case.k_cache), D.t(case.v_cache)
@@ -83,11 +126,15 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False):
     ws = pa.decode_workspace(q.shape[0], case.max_seq_len, case.block_size, device=D.dev)
     out = torch.empty_like(q)
 
-    def step(i):
+    def step(i, ev=None):
         r = i % reps
         if has_write:
             pa.kv_write_fused(ks[r], vs[r], kn, vn, pos, bt, seq)
+        if ev is not None:
+            ev[0].record()
         pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+        if ev is not None:
+            ev[1].record()
 
     for i in range(warmup):
         step(i)
@@ -95,7 +142,7 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False):
     res = {"replicas": reps}
     nbytes = kv_bytes(case.seq_lens)
     if graph:
-        # one graph holds one step per replica; replayed steps // reps times
+        # one graph holds one step per replica; replayed until >= steps steps ran
         g = torch.cuda.CUDAGraph()
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
@@ -104,7 +151,7 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False):
                 for i in range(reps):
                     step(i)
         torch.cuda.current_stream().wait_stream(s)
-        n_rep = max(1, steps // reps)
+        n_rep = max(1, -(-steps // reps))
         g.replay()
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -114,30 +161,16 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False):
         e1.record()
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / (n_rep * reps)
-        res.update(ms_per_step=ms, gbs=nbytes / (ms * 1e-3) / 1e9)
+        res.update(ms_per_step=ms, steps=n_rep * reps, gbs=nbytes / (ms * 1e-3) / 1e9)
         return res
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for i in range(steps):
-        r = i % reps
-        if has_write:
-            pa.kv_write_fused(ks[r], vs[r], kn, vn, pos, bt, seq)
-        evs[i][0].record()
-        pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
-        evs[i][1].record()
-    e1.record()
-    torch.cuda.synchronize()
-    total_ms = e0.elapsed_time(e1)
-    kern = sorted(a.elapsed_time(b) for a, b in evs)
-    avg_kernel_ms = sum(kern) / len(kern)
-    res.update(ms_per_step=total_ms / steps, kernel_ms_avg=avg_kernel_ms,
-               kernel_ms_p10=kern[len(kern) // 10], kernel_ms_p50=kern[len(kern) // 2],
-               kernel_ms_p90=kern[(9 * len(kern)) // 10],
-               kv_bytes=nbytes, gbs=nbytes / (total_ms / steps * 1e-3) / 1e9,
-               kernel_gbs=nbytes / (avg_kernel_ms * 1e-3) / 1e9)
+    hold = hold_ms if hold_ms is not None else 0.25 * steps + 20
+    total_ms, kern, host_s = timed_loop(torch, steps, step, hold)
+    st = _stats(kern)
+    res.update(ms_per_step=total_ms / steps, kv_bytes=nbytes,
+               gbs=nbytes / (total_ms / steps * 1e-3) / 1e9,
+               kernel_gbs=nbytes / (st["kernel_ms_avg"] * 1e-3) / 1e9,
+               host_enqueue_ms=host_s * 1e3, hold_ms=hold,
+               host_bound=bool(host_s * 1e3 > hold), **st)
     return res
 
 
@@ -159,22 +192,20 @@ def bench_prefill(D, pa, case, steps, warmup):
         w1.record()
         for _ in range(warmup):
             pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
-        torch.cuda.synchronize()
-        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(steps)]
-        for i in range(steps):
-            evs[i][0].record()
+
+        def step(i, ev):
+            ev[0].record()
             pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
-            evs[i][1].record()
-        torch.cuda.synchronize()
-        t = sorted(a.elapsed_time(b) for a, b in evs)
-        avg = sum(t) / len(t)
+            ev[1].record()
+
+        total_ms, kern, host_s = timed_loop(torch, steps, step, 5.0)
+        st = _stats(kern)
+        avg = st["kernel_ms_avg"]
         fl = causal_flops(ch.start_pos, ch.q_len)
-        out[f"q{ch.q_len}_start{ch.start_pos}"] = {
-            "kernel_ms_avg": avg, "kernel_ms_p10": t[len(t) // 10], "kernel_ms_p50": t[len(t) // 2],
-            "kernel_ms_p90": t[(9 * len(t)) // 10], "causal_flops": fl,
-            "tflops": fl / (avg * 1e-3) / 1e12, "frac_bf16_peak": fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "kv_write_ms": w0.elapsed_time(w1), "kv_write_bytes": ch.q_len * 4 * 256 * 2 * 2}
+        out[f"q{ch.q_len}_start{ch.start_pos}"] = dict(
+            st, causal_flops=fl, tflops=fl / (avg * 1e-3) / 1e12,
+            frac_bf16_peak=fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            kv_write_ms=w0.elapsed_time(w1), kv_write_bytes=ch.q_len * 4 * 256 * 2 * 2)
     return out
 
 

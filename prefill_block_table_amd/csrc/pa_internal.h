@@ -28,7 +28,9 @@ struct DecodePlan {
   int32_t units_per_page;
   int32_t groups_per_split;
   int32_t max_splits;       // splits of the longest sequence (grid x)
-  size_t counters_off, ml_off, acc_off, bytes;
+  int32_t cluster;          // splits merged together at the first merge level
+  int32_t max_clusters;     // clusters of the longest sequence
+  size_t cnt1_off, cnt2_off, p1_ml_off, p2_ml_off, p1_acc_off, p2_acc_off, bytes;
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
