@@ -21,16 +21,17 @@ hipError_t launch_kv_write(uint16_t* k_cache, uint16_t* v_cache, int64_t page_st
                            const int32_t* token_seq, const int32_t* block_table,
                            int32_t bt_stride, int64_t* slot_out, hipStream_t stream);
 
-// Split-K plan of a decode batch: a "unit" is one 64-token group of one page
-// (a page of B tokens has ceil(B / 64) units, the last one a tail when B is
-// not a multiple of 64); a split is `groups_per_split` consecutive units.
+// Decode split plan.  A step is 16 tokens of one page for `heads_per_wg`
+// KV heads (16 * 4 / heads_per_wg tokens when a workgroup's four waves share
+// fewer heads).  The batch's steps are cut into `num_wgs` near-equal ranges.
+constexpr int kDecodeWorkgroups = 256;   // one per MI355X CU
+
 struct DecodePlan {
-  int32_t units_per_page;
-  int32_t groups_per_split;
-  int32_t max_splits;       // splits of the longest sequence (grid x)
-  int32_t cluster;          // splits merged together at the first merge level
-  int32_t max_clusters;     // clusters of the longest sequence
-  size_t cnt1_off, cnt2_off, p1_ml_off, p2_ml_off, p1_acc_off, p2_acc_off, bytes;
+  int32_t heads_per_wg;
+  int32_t step_tokens;
+  int32_t steps_per_page;
+  int32_t num_wgs;
+  size_t meta_off, p_ml_off, p_acc_off, bytes;
 };
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
