@@ -33,8 +33,7 @@
  *    a multiple of 64 cost one masked tail group per page.
  *  - Ownership: the caller owns every buffer, including the decode
  *    workspace.  The library never allocates or frees device memory and
- *    keeps no state between calls (the workspace's counters are left at zero
- *    by each completed call).
+ *    keeps no state between calls.
  *  - Execution: each call validates its arguments on the host, then only
  *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
  *    returns without synchronizing.  On any error nothing is enqueued.
@@ -117,13 +116,11 @@ int pa_kv_write_fused(uint16_t* k_cache, uint16_t* v_cache, int64_t page_stride,
                       void* stream);
 
 /*
- * Bytes of device workspace pa_decode needs for this batch shape.  The
- * workspace holds split-K partial results and one arrival counter per
- * (sequence, KV head).  It must be zero-filled once before its first use;
- * every completed pa_decode call leaves its counters at zero again, so it
- * can be reused by later calls of the same or smaller shape on the same
- * stream.  Two pa_decode calls that share a workspace must not overlap.
- * bytes_out: host pointer.
+ * Bytes of device workspace pa_decode needs for this batch shape (split-K
+ * partial results and per-sequence merge metadata).  The workspace needs no
+ * initialisation: every pa_decode call writes what it later reads.  Two
+ * pa_decode calls that share a workspace must not run concurrently (calls
+ * queued on one stream are fine).  bytes_out: host pointer.
  * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE.
  */
 int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
@@ -147,7 +144,7 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t bloc
  * max_seq_len   host-side bound on seq_lens, >= 1, and
  *               <= bt_stride * block_size.
  * workspace     device buffer of >= pa_decode_workspace_size(...) bytes,
- *               zero-filled before first use (see above).
+ *               256-byte aligned, contents arbitrary (see above).
  * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE
  * (num_seqs < 1, max_seq_len < 1), PA_ERR_TABLE, PA_ERR_STRIDE,
  * PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_LAUNCH.

@@ -165,8 +165,8 @@ def decode_workspace_size(num_seqs: int, max_seq_len: int, block_size: int,
 
 def decode_workspace(num_seqs: int, max_seq_len: int, block_size: int, num_kv_heads: int = 4,
                      device="cuda") -> torch.Tensor:
-    """A zero-filled workspace of the size pa_decode needs (reusable)."""
-    return torch.zeros(decode_workspace_size(num_seqs, max_seq_len, block_size, num_kv_heads),
+    """A workspace of the size pa_decode needs (reusable; no initialisation needed)."""
+    return torch.empty(decode_workspace_size(num_seqs, max_seq_len, block_size, num_kv_heads),
                        dtype=torch.uint8, device=device)
 
 

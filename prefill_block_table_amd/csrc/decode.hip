@@ -190,7 +190,6 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
   const int stok = a.step_tokens;
   const int c16 = lane & 15;
   const int kq = lane >> 4;
-  const int64_t N = a.num_wgs;
 
   // Total steps T of the batch, this workgroup's range [x0, x1) and the
   // sequence holding step x0.  One pass over seq_lens when the batch has at
@@ -203,6 +202,11 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
     T += block_sum(v, red);
   }
   if (T == 0) return;
+  // Effective workgroup count min(launched, T): every workgroup below it owns
+  // at least one step, so the workgroups sharing an item are consecutive and
+  // its partials occupy consecutive slots.
+  const int64_t N = T < a.num_wgs ? T : a.num_wgs;
+  if (wgi >= N) return;
   const int64_t x0 = wg_bound(wgi, T, N);
   const int64_t x1 = wg_bound(wgi + 1, T, N);
   if (x0 >= x1) return;
@@ -530,7 +534,10 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
 
   // One pass: each slice keeps its own running max.
   float M = -INFINITY, O = 0.f, Ls = 0.f;
-  constexpr int kUnroll = 8;
+#ifndef PA_MERGE_UNROLL
+#define PA_MERGE_UNROLL 8
+#endif
+  constexpr int kUnroll = PA_MERGE_UNROLL;
   for (int p0 = z; p0 < nparts; p0 += kMergeSlices * kUnroll) {
     float mv[kUnroll], lv[kUnroll], av[kUnroll];
 #pragma unroll
@@ -587,7 +594,11 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
                        int32_t num_kv_heads) {
   DecodePlan p{};
+#ifdef PA_DECODE_HPW
+  p.heads_per_wg = PA_DECODE_HPW;
+#else
   p.heads_per_wg = num_kv_heads % 4 == 0 ? 4 : (num_kv_heads % 2 == 0 ? 2 : 1);
+#endif
   p.step_tokens = 16 * (kWaves / p.heads_per_wg);
   p.steps_per_page = (block_size + p.step_tokens - 1) / p.step_tokens;
   const int64_t items = (int64_t)num_seqs * (num_kv_heads / p.heads_per_wg);

@@ -125,6 +125,19 @@ def test_single_kv_head_shard():
     compare(run_gpu(c), run_oracle(c), c.name)
 
 
+def test_workspace_contents_never_read_uninitialised():
+    """The workspace needs no initialisation: fill it with NaN bytes first."""
+    import torch
+    pa = _pa()
+    for B, lens in ((64, [1, 2, 15, 17, 63, 65, 129, 191]), (832, [8193]), (16, [3, 4000, 70])):
+        c = W.make_decode_case(f"ws_poison_b{B}", 90 + B, lens, B,
+                               sum(-(-n // B) for n in lens) + 3, write_new_token=False)
+        ws = pa.decode_workspace(len(lens), c.max_seq_len, B, device="cuda")
+        ws.fill_(0xFF)                     # every float / int in it reads as NaN / -1
+        log(f"{c.name} lens={lens}")
+        compare(run_gpu(c, ws=ws), run_oracle(c), c.name)
+
+
 def test_workspace_reuse_across_shapes():
     """A workspace sized for a large batch serves later, smaller calls."""
     pa = _pa()
