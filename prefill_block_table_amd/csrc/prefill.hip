@@ -10,14 +10,18 @@
 // 64-token group of one page at a time (the page's tail group is masked when
 // the page size is not a multiple of 64).  Per group:
 //   S^T[64 keys x 32 rows] = K[64 x 256] Q^T     (32 MFMA 32x32x16 per wave)
-//   online softmax on S^T: each lane holds one query row, so the row max and
-//   sum need one cross-lane exchange (lane ^ 32) only
+//   online softmax on S^T: each lane holds one query row, so the row max
+//   needs one cross-lane exchange (lane ^ 32); the accumulator is re-based
+//   only when the max grows by more than 2^8
 //   O^T[256 x 32 rows] += V^T[256 x 64] P^T     (32 MFMA 32x32x16 per wave)
 // The transposed orientation makes P^T's MFMA operand a register-local
-// reinterpretation of S^T's accumulator (no shuffles); V is transposed once
-// while it is staged into LDS.  Groups entirely above the causal diagonal of
-// the tile are never visited; the mask is evaluated only on groups that
-// cross the diagonal or end a page early.
+// reinterpretation of S^T's accumulator.  K and V rows go from HBM straight
+// into LDS with the direct-to-LDS load, double-buffered (the next group is in
+// flight while this one is computed), 16-byte chunks XOR-swizzled by row so
+// operand reads are bank-conflict free; V^T operands come out of LDS with the
+// gfx950 transposing read.  Groups entirely above the causal diagonal of the
+// tile are never visited; the mask is evaluated only on groups that cross the
+// diagonal or end a page early.
 #include <math.h>
 
 #include "pa_device.h"
@@ -25,13 +29,20 @@
 
 namespace pa {
 
-const char* const kPrefillVariant = "prefill-v1(bm128,bn64,mfma32x32x16,st-orient,lds-vt,heavy-first)";
+const char* const kPrefillVariant =
+    "prefill-v2(bm128,bn64,mfma32x32x16,st-orient,lds-dma-kv,2stage,tr16-vt,lazy-rescale,heavy-first)";
 
 namespace {
 
 constexpr int kBM = 128;
-constexpr int kKStride = kHeadDim + 8;  // bf16 elements per K row in LDS (16 B pad)
-constexpr int kVtStride = kGroup + 4;   // bf16 elements per V^T row in LDS (8 B pad)
+constexpr int kRowBytes = kHeadDim * 2;             // one KV head's row: 512 B
+constexpr int kTileBytes = kGroup * kRowBytes;      // 64 rows: 32 KB
+constexpr int kStageBytes = 2 * kTileBytes;         // K tile then V tile
+constexpr int kSmemBytes = 2 * kStageBytes;         // two stages: 128 KB
+constexpr float kRescaleSlack = 8.f;
+
+#define PA_LDS __attribute__((address_space(3)))
+#define PA_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 
 struct PrefillArgs {
   uint16_t* out;
@@ -53,9 +64,34 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const PA_LDS char*)p;
+}
+
+__device__ __forceinline__ int32_t load_const_i32(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// 16-byte chunk c of K row r at position c ^ (r & 15): the 16 rows one
+// operand read touches at a time hit 16 different bank quads.  V row r: chunk
+// c at c ^ ((r & 7) << 2): the 8 rows x 64 bytes of one transposing read are
+// spread over the banks.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return (r & 7) << 2; }
+
+// LDS reads the compiler does not track (it cannot tell which direct-to-LDS
+// load wrote which bytes and would drain the prefetched group before every
+// read); callers order them with explicit waits.
+#define PA_DS_READ_B128(dst, addr) asm volatile("ds_read_b128 %0, %1" : "=v"(dst) : "v"(addr))
+#define PA_DS_READ_TR16(dst, addr) asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(dst) : "v"(addr))
+
 __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kGroup * kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kHeadDim * kVtStride];
+  __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
 
   const int head = blockIdx.x;
   const int tile = a.num_q_tiles - 1 - (int)blockIdx.y;   // heaviest (latest) rows first
@@ -101,123 +137,193 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
   for (int db = 0; db < 8; ++db)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
-  float m_run = -INFINITY;
-  float l_run = 0.f;
+  float m_run = -INFINITY;    // reference the accumulator is scaled to
+  float l_run = 0.f;          // this lane's partial row sum (its 32 keys per group)
 
-  for (int u = 0; u < units; ++u) {
+  const char* kbase_g = reinterpret_cast<const char*>(a.k_cache + (int64_t)g * kHeadDim);
+  const char* vbase_g = reinterpret_cast<const char*>(a.v_cache + (int64_t)g * kHeadDim);
+  const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
+
+  // Issue group u into a stage: this wave loads rows 16w .. 16w+15 of K and V
+  // (8 + 8 direct-to-LDS loads of two rows each).  Rows past the group's live
+  // end reload the page's first row (finite; masked out).
+  auto issue = [&](int u, char* st) {
     const int page = u / upp;
     const int grp = u - page * upp;
-    const int key0 = page * B + grp * kGroup;                 // absolute position of key 0
+    const int key0 = page * B + grp * kGroup;
     const int n = min(kGroup, min(B - grp * kGroup, kv_end - key0));
-    const int64_t phys = a.block_table[page];
-    const int64_t off = phys * a.page_stride + (int64_t)grp * kGroup * row_stride + (int64_t)g * kHeadDim;
-    const uint16_t* kg = a.k_cache + off;
-    const uint16_t* vg = a.v_cache + off;
+    const int64_t poff = (int64_t)load_const_i32(a.block_table + page) * a.page_stride * 2 +
+                         (int64_t)grp * kGroup * rs_bytes;
+    const char* kp = kbase_g + poff;
+    const char* vp = vbase_g + poff;
+    const int pos = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int row = 16 * w + 2 * j + (lane >> 5);
+      // signed: a masked row points back at the page's first row
+      const int32_t roff = (row < n ? row : -grp * kGroup) * (int32_t)rs_bytes;
+      __builtin_amdgcn_global_load_lds(kp + roff + ((pos ^ kswz(row)) << 4),
+                                       (PA_LDS void*)(st + row * kRowBytes - (lane >> 5) * kRowBytes),
+                                       16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vp + roff + ((pos ^ vswz(row)) << 4),
+                                       (PA_LDS void*)(st + kTileBytes + row * kRowBytes - (lane >> 5) * kRowBytes),
+                                       16, 0, 0);
+    }
+  };
 
-    __syncthreads();   // all waves are done reading the previous group
-    // K rows -> LDS (64 rows x 32 vectors of 16 B).
-#pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int c = it * 256 + tid;
-      const int row = c >> 5;
-      const int ch = c & 31;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row < n) v = load16(kg + (int64_t)row * row_stride + 8 * ch);
-      *reinterpret_cast<u32x4*>(&k_lds[row * kKStride + 8 * ch]) = v;
-    }
-    // V rows -> V^T in LDS: each thread takes 4 keys x 8 dims and writes 8
-    // rows of V^T, 4 keys (8 B) each.
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int c = it * 256 + tid;
-      const int kq = c >> 5;          // key quad 0..15
-      const int dc = c & 31;          // 8-dim chunk 0..31
-      u32x4 r4[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = 4 * kq + i;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (row < n) v = load16(vg + (int64_t)row * row_stride + 8 * dc);
-        r4[i] = v;
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int wd = dd >> 1;
-        const int sh = (dd & 1) * 16;
-        const uint32_t e0 = (r4[0][wd] >> sh) & 0xffffu;
-        const uint32_t e1 = (r4[1][wd] >> sh) & 0xffffu;
-        const uint32_t e2 = (r4[2][wd] >> sh) & 0xffffu;
-        const uint32_t e3 = (r4[3][wd] >> sh) & 0xffffu;
-        u32x2 pk = {e0 | (e1 << 16), e2 | (e3 << 16)};
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * dc + dd) * kVtStride + 4 * kq]) = pk;
-      }
-    }
-    __syncthreads();
+  char* st0 = smem;
+  char* st1 = smem + kStageBytes;
+  issue(0, st0);
 
-    // S^T = K Q^T for keys 0..31 (st0) and 32..63 (st1).
-    f32x16 st0, st1;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) { st0[r] = 0.f; st1[r] = 0.f; }
-#pragma unroll
-    for (int ds = 0; ds < 16; ++ds) {
-      const bf16x8 ka0 = *reinterpret_cast<const bf16x8*>(&k_lds[col * kKStride + 16 * ds + 8 * hh]);
-      const bf16x8 ka1 = *reinterpret_cast<const bf16x8*>(&k_lds[(32 + col) * kKStride + 16 * ds + 8 * hh]);
-      st0 = mfma32(ka0, qb[ds], st0);
-      st1 = mfma32(ka1, qb[ds], st1);
+  for (int u = 0; u < units; ++u) {
+    char* st = (u & 1) ? st1 : st0;
+    if (u + 1 < units) {
+      issue(u + 1, (u & 1) ? st0 : st1);
+      PA_WAIT_VMCNT(16);      // this wave's part of group u has landed
+    } else {
+      PA_WAIT_VMCNT(0);
     }
-    // Accumulator register r of st{kh} holds key 32*kh + 8*(r/4) + 4*hh + r%4
-    // for query row `col` of this wave.
-    float sv[32];
+    __syncthreads();          // every wave's part of group u has landed
+
+    const int page = u / upp;
+    const int grp = u - page * upp;
+    const int key0 = page * B + grp * kGroup;
+    const int n = min(kGroup, min(B - grp * kGroup, kv_end - key0));
+    const uint32_t kt = lds_addr(st);
+    const uint32_t vt = kt + kTileBytes;
+
+    // S^T = K Q^T for keys 0..31 (s0) and 32..63 (s1).  A operand: key row
+    // 32*kh + col, 16-byte chunk 2*ds + hh.  LDS reads run one batch (two
+    // d-steps) ahead of the MFMAs (lgkmcnt(4) keeps the newer batch in flight).
+    f32x16 s0, s1;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) { sv[r] = st0[r] * a.scale_log2; sv[16 + r] = st1[r] * a.scale_log2; }
+    for (int r = 0; r < 16; ++r) { s0[r] = 0.f; s1[r] = 0.f; }
+    {
+      const uint32_t ka0 = kt + col * kRowBytes;
+      const uint32_t ka1 = kt + (32 + col) * kRowBytes;
+      const int sw = kswz(col);      // (32 + col) & 15 == col & 15
+      u32x4 kb[2][4];
+      auto kread = [&](int ds, u32x4& d0, u32x4& d1) {
+        PA_DS_READ_B128(d0, ka0 + (((2 * ds + hh) ^ sw) << 4));
+        PA_DS_READ_B128(d1, ka1 + (((2 * ds + hh) ^ sw) << 4));
+      };
+      kread(0, kb[0][0], kb[0][1]);
+      kread(1, kb[0][2], kb[0][3]);
+#pragma unroll
+      for (int bt = 0; bt < 8; ++bt) {
+        const int cur = bt & 1;
+        if (bt < 7) {
+          kread(2 * bt + 2, kb[cur ^ 1][0], kb[cur ^ 1][1]);
+          kread(2 * bt + 3, kb[cur ^ 1][2], kb[cur ^ 1][3]);
+          asm volatile("s_waitcnt lgkmcnt(4)"
+                       : "+v"(kb[cur][0]), "+v"(kb[cur][1]), "+v"(kb[cur][2]), "+v"(kb[cur][3]));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(kb[cur][0]), "+v"(kb[cur][1]), "+v"(kb[cur][2]), "+v"(kb[cur][3]));
+        }
+        s0 = mfma32(as_bf16x8(kb[cur][0]), qb[2 * bt], s0);
+        s1 = mfma32(as_bf16x8(kb[cur][1]), qb[2 * bt], s1);
+        s0 = mfma32(as_bf16x8(kb[cur][2]), qb[2 * bt + 1], s0);
+        s1 = mfma32(as_bf16x8(kb[cur][3]), qb[2 * bt + 1], s1);
+      }
+    }
+
+    // Accumulator register r of s{kh} holds key 32*kh + 8*(r/4) + 4*hh + r%4
+    // for query row `col` of this wave.  Scaled in place.
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { s0[r] *= a.scale_log2; s1[r] *= a.scale_log2; }
     const bool need_mask = (n < kGroup) || (a.causal && key0 + kGroup - 1 > wave_first_pos);
     if (need_mask) {
 #pragma unroll
-      for (int r = 0; r < 32; ++r) {
-        const int key = (r >> 4) * 32 + 8 * ((r & 15) >> 2) + 4 * hh + (r & 3);
-        if (key >= n || (a.causal && key0 + key > my_pos)) sv[r] = -INFINITY;
+      for (int r = 0; r < 16; ++r) {
+        const int key_lo = 8 * (r >> 2) + 4 * hh + (r & 3);
+        if (key_lo >= n || (a.causal && key0 + key_lo > my_pos)) s0[r] = -INFINITY;
+        if (key_lo + 32 >= n || (a.causal && key0 + key_lo + 32 > my_pos)) s1[r] = -INFINITY;
       }
     }
-    float mx = sv[0];
+    float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
-    for (int r = 1; r < 32; ++r) mx = fmaxf(mx, sv[r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_use);
-    m_run = m_new;
-    float rs = 0.f;
+    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
+    mx = pair32_max(mx);
+    if (__any(mx > m_run + kRescaleSlack)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+#pragma unroll
+      for (int db = 0; db < 8; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
+    // pk[i] packs the weights of accumulator registers 2i, 2i+1 (s0: i < 8, s1: i >= 8)
     uint32_t pk[16];
+    float rs = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float p0 = fast_exp2(sv[2 * i] - m_use);
-      const float p1 = fast_exp2(sv[2 * i + 1] - m_use);
-      rs += p0 + p1;
+    for (int i = 0; i < 8; ++i) {
+      const float p0 = fast_exp2(s0[2 * i] - m_use);
+      const float p1 = fast_exp2(s0[2 * i + 1] - m_use);
+      const float p2 = fast_exp2(s1[2 * i] - m_use);
+      const float p3 = fast_exp2(s1[2 * i + 1] - m_use);
+      rs += (p0 + p1) + (p2 + p3);
       pk[i] = pack_bf16x2(p0, p1);
+      pk[8 + i] = pack_bf16x2(p2, p3);
     }
-    l_run = l_run * alpha + rs;
-#pragma unroll
-    for (int db = 0; db < 8; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+    l_run += rs;
 
-    // O^T += V^T P^T over 4 steps of 16 keys.  MFMA k = 8*hh + 4*jj + i maps
-    // to key 16*ks + 8*jj + 4*hh + i on both operands.
+    // O^T += V^T P^T over 4 steps of 16 keys.  MFMA k = 8*hh + 4*jj + e maps
+    // to key 16*ks + 8*jj + 4*hh + e on both operands.  V^T operand: two
+    // transposing reads, lane group (hh, dsub = lane/16 & 1) pointing at
+    // V[key0 + (j >> 2)][d0 + 4*(j & 3)], key0 = 16*ks + 8*jj + 4*hh,
+    // d0 = 32*db + 16*dsub (j = lane % 16).
+    {
+      const int j16 = lane & 15;
+      const int dsub = (lane >> 4) & 1;
+      const int vrow_lo = 4 * hh + (j16 >> 2);          // + 16*ks + 8*jj
+      const uint32_t dofs = (uint32_t)(16 * dsub + 4 * (j16 & 3)) * 2;   // bytes within 32-d block
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const int kh = ks >> 1;
-      const int j0 = 2 * (ks & 1);
-      const u32x4 pb = {pk[8 * kh + 2 * j0], pk[8 * kh + 2 * j0 + 1],
-                        pk[8 * kh + 2 * j0 + 2], pk[8 * kh + 2 * j0 + 3]};
+      for (int ks = 0; ks < 4; ++ks) {
+        const int kh = ks >> 1;
+        const int j0 = 2 * (ks & 1);
+        const u32x4 pb = {pk[8 * kh + 2 * j0], pk[8 * kh + 2 * j0 + 1],
+                          pk[8 * kh + 2 * j0 + 2], pk[8 * kh + 2 * j0 + 3]};
+        const int r0 = 16 * ks + vrow_lo;       // jj = 0
+        const int r1 = r0 + 8;                  // jj = 1
+        const uint32_t v0 = vt + r0 * kRowBytes;
+        const uint32_t v1 = vt + r1 * kRowBytes;
+        const int sw0 = vswz(r0), sw1 = vswz(r1);
+        u32x2 va[2][4][2];
+        auto vread = [&](int db, u32x2 (&dst)[2]) {
+          const uint32_t byte = (uint32_t)db * 64 + dofs;   // 32 d = 64 bytes per block
+          const uint32_t ch = byte >> 4, lo = byte & 15;
+          PA_DS_READ_TR16(dst[0], v0 + ((ch ^ sw0) << 4) + lo);
+          PA_DS_READ_TR16(dst[1], v1 + ((ch ^ sw1) << 4) + lo);
+        };
 #pragma unroll
-      for (int db = 0; db < 8; ++db) {
-        const uint16_t* vrow = &vt_lds[(32 * db + col) * kVtStride + 16 * ks + 4 * hh];
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vrow);
-        const u32x2 a1 = *reinterpret_cast<const u32x2*>(vrow + 8);
-        const u32x4 va = {a0[0], a0[1], a1[0], a1[1]};
-        o[db] = mfma32(as_bf16x8(va), as_bf16x8(pb), o[db]);
+        for (int i = 0; i < 4; ++i) vread(i, va[0][i]);
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          if (half == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) vread(4 + i, va[1][i]);
+            asm volatile("s_waitcnt lgkmcnt(8)"
+                         : "+v"(va[0][0][0]), "+v"(va[0][0][1]), "+v"(va[0][1][0]), "+v"(va[0][1][1]),
+                           "+v"(va[0][2][0]), "+v"(va[0][2][1]), "+v"(va[0][3][0]), "+v"(va[0][3][1]));
+          } else {
+            asm volatile("s_waitcnt lgkmcnt(0)"
+                         : "+v"(va[1][0][0]), "+v"(va[1][0][1]), "+v"(va[1][1][0]), "+v"(va[1][1][1]),
+                           "+v"(va[1][2][0]), "+v"(va[1][2][1]), "+v"(va[1][3][0]), "+v"(va[1][3][1]));
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int db = 4 * half + i;
+            const u32x4 av = {va[half][i][0][0], va[half][i][0][1], va[half][i][1][0], va[half][i][1][1]};
+            o[db] = mfma32(as_bf16x8(av), as_bf16x8(pb), o[db]);
+          }
+        }
       }
     }
+    __syncthreads();          // all waves are done with this stage before it is refilled
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
