@@ -26,6 +26,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor spec
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ctx8192_b832_hbm_traffic.json")
+DECODE_SRC = os.path.join(ROOT, "prefill_block_table_amd", "csrc", "decode.hip")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor spec
 MALL_DEFEAT_BYTES = 2 << 30    # rotate pool replicas over at least this many bytes
 
@@ -38,6 +40,9 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--counter-pass", action="store_true",
+                    help="for rocprofv3 --pmc runs: a few headline decode steps, then a "
+                         "256 MiB device-to-device copy that calibrates FETCH_SIZE/WRITE_SIZE")
     return ap.parse_args()
 
 
@@ -83,11 +88,11 @@ def gpu_hold(torch, ms):
     torch.cuda._sleep(int(_SLEEP_CYCLES_PER_MS * ms))
 
 
-def timed_loop(torch, steps, launch_step, hold_ms):
+def timed_loop(torch, steps, launch_step, hold_ms, events=True):
     """Run `steps` steps after a GPU hold; returns (total_ms, per-step kernel
-    ms of the bracketed launch, host enqueue seconds)."""
+    ms of the bracketed launch (empty without events), host enqueue seconds)."""
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(steps)]
+           if events else None for _ in range(steps)]
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     gpu_hold(torch, hold_ms)
@@ -98,7 +103,7 @@ def timed_loop(torch, steps, launch_step, hold_ms):
     e1.record()
     host_s = time.perf_counter() - t0
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1), [a.elapsed_time(b) for a, b in evs], host_s
+    return e0.elapsed_time(e1), ([a.elapsed_time(b) for a, b in evs] if events else []), host_s
 
 
 def _stats(ts):
@@ -164,13 +169,21 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=N
         res.update(ms_per_step=ms, steps=n_rep * reps, gbs=nbytes / (ms * 1e-3) / 1e9)
         return res
     hold = hold_ms if hold_ms is not None else 0.25 * steps + 20
-    total_ms, kern, host_s = timed_loop(torch, steps, step, hold)
+    # 1) whole steps, nothing between the launches
+    total_ms, _, host_s = timed_loop(torch, steps, lambda i, ev: step(i), hold, events=False)
+    # 2) the decode call alone (split + merge kernels), bracketed by events
+    def dec_only(i, ev):
+        r = i % reps
+        ev[0].record()
+        pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+        ev[1].record()
+    _, kern, host_k = timed_loop(torch, steps, dec_only, hold)
     st = _stats(kern)
     res.update(ms_per_step=total_ms / steps, kv_bytes=nbytes,
                gbs=nbytes / (total_ms / steps * 1e-3) / 1e9,
                kernel_gbs=nbytes / (st["kernel_ms_avg"] * 1e-3) / 1e9,
                host_enqueue_ms=host_s * 1e3, hold_ms=hold,
-               host_bound=bool(host_s * 1e3 > hold), **st)
+               host_bound=bool(max(host_s, host_k) * 1e3 > hold), **st)
     return res
 
 
@@ -207,6 +220,49 @@ def bench_prefill(D, pa, case, steps, warmup):
             frac_bf16_peak=fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             kv_write_ms=w0.elapsed_time(w1), kv_write_bytes=ch.q_len * 4 * 256 * 2 * 2)
     return out
+
+
+def decode_src_sha():
+    import hashlib
+    with open(DECODE_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per pa_decode launch from the committed counter runs, or None
+    when the decode kernels changed since those counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("decode_src_sha") != decode_src_sha():
+        return None
+    return t.get("hbm_bytes_per_launch")
+
+
+def counter_pass(D, pa, W):
+    """Launch sequence profiled by the --pmc runs: 10 headline decode steps on
+    distinct pool replicas, then a plain 256 MiB copy of known size."""
+    torch = D.torch
+    case = W.decode_8k()
+    k0, v0 = D.t(case.k_cache), D.t(case.v_cache)
+    bt, sl, q = D.t(case.block_tables), D.t(case.seq_lens), D.t(case.q)
+    kn, vn = D.t(case.k_new), D.t(case.v_new)
+    pos, seq = D.t(case.positions), D.t(case.token_seq)
+    ws = pa.decode_workspace(1, case.max_seq_len, case.block_size, device=D.dev)
+    out = torch.empty_like(q)
+    for _ in range(10):
+        k, v = k0.clone(), v0.clone()           # fresh replica: cold in L2 and MALL
+        torch.cuda.synchronize()
+        pa.kv_write_fused(k, v, kn, vn, pos, bt, seq)
+        pa.decode(q, k, v, bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+        torch.cuda.synchronize()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=D.dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
 
 
 def cpu_baseline(case, seconds):
@@ -246,6 +302,9 @@ def main():
         sys.exit(1)
     D = Dev()
     print(f"[bench] {pa.build_info()}", file=sys.stderr, flush=True)
+    if args.counter_pass:
+        counter_pass(D, pa, W)
+        return
 
     head_case = W.decode_8k()
     print("[bench] decode_ctx8192_b832 rotated", file=sys.stderr, flush=True)
@@ -294,8 +353,11 @@ def main():
                                "pool 64 pages, 24 q / 4 KV heads, head_dim 256",
                    "kv_bytes_per_step": head["kv_bytes"], "pool_replicas": head["replicas"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "decode_kernel", "kernel_ms_avg": head["kernel_ms_avg"]},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(),
+                     "kernel": "pa_decode (decode_split_kernel + decode_merge_kernel)",
+                     "launch_ms_avg": round(head["kernel_ms_avg"], 6),
+                     "algorithmic_bytes_per_launch": head["kv_bytes"]},
         "cpu_baseline": cpu,
         "extra": extra,
     }
