@@ -3,10 +3,10 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W]
 
-One step = one decode step of the 8K-context workload: the fused
-slot-mapping KV-cache write of the new token (position 8192) followed by the
-split-K decode over its 8193 keys (page 832, 24 query / 4 KV heads, head 256,
-bf16).  `value` is decode K/V bytes moved per second over the whole timed
+One step = one decode step of the 8K-context workload: the slot-mapping
+KV-cache write of the new token (position 8192) and the split-K decode over
+its 8193 keys (page 832, 24 query / 4 KV heads, head 256, bf16), issued as one
+pa_decode_append call (the write happens inside the decode launch).  `value` is decode K/V bytes moved per second over the whole timed
 region (K/V bytes = seq_len * 4 heads * 256 * 2 B * 2 for K and V); each step
 reads a different replica of the KV pool so that the reads come from HBM,
 not from the 256 MB Infinity Cache.  The same run also measures the other
@@ -112,8 +112,11 @@ def _stats(ts):
             "kernel_ms_p50": t[len(t) // 2], "kernel_ms_p90": t[(9 * len(t)) // 10]}
 
 
-def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=None):
-    """Timed decode steps (KV write of the new token + decode); returns a dict."""
+def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=None,
+                 separate=False):
+    """Timed decode steps (KV write of the new token + decode); returns a dict.
+    A step is one decode_append call, or with `separate` a kv_write_fused call
+    followed by a decode call."""
     torch = D.torch
     k0, v0 = D.t(case.k_cache), D.t(case.v_cache)
     pool_bytes = 2 * k0.numel() * 2
@@ -133,13 +136,13 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=N
 
     def step(i, ev=None):
         r = i % reps
+        if has_write and not separate:
+            pa.decode_append(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, kn, vn,
+                             workspace=ws, out=out)
+            return
         if has_write:
             pa.kv_write_fused(ks[r], vs[r], kn, vn, pos, bt, seq)
-        if ev is not None:
-            ev[0].record()
         pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(warmup):
         step(i)
@@ -175,11 +178,18 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=N
     def dec_only(i, ev):
         r = i % reps
         ev[0].record()
-        pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+        if has_write and not separate:
+            pa.decode_append(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, kn, vn,
+                             workspace=ws, out=out)
+        else:
+            pa.decode(q, ks[r], vs[r], bt, sl, case.max_seq_len, case.scale, workspace=ws,
+                      out=out)
         ev[1].record()
     _, kern, host_k = timed_loop(torch, steps, dec_only, hold)
     st = _stats(kern)
-    res.update(ms_per_step=total_ms / steps, kv_bytes=nbytes,
+    res.update(call="decode_append" if has_write and not separate else
+               ("kv_write_fused + decode" if has_write else "decode"),
+               ms_per_step=total_ms / steps, kv_bytes=nbytes,
                gbs=nbytes / (total_ms / steps * 1e-3) / 1e9,
                kernel_gbs=nbytes / (st["kernel_ms_avg"] * 1e-3) / 1e9,
                host_enqueue_ms=host_s * 1e3, hold_ms=hold,
@@ -249,14 +259,13 @@ def counter_pass(D, pa, W):
     k0, v0 = D.t(case.k_cache), D.t(case.v_cache)
     bt, sl, q = D.t(case.block_tables), D.t(case.seq_lens), D.t(case.q)
     kn, vn = D.t(case.k_new), D.t(case.v_new)
-    pos, seq = D.t(case.positions), D.t(case.token_seq)
     ws = pa.decode_workspace(1, case.max_seq_len, case.block_size, device=D.dev)
     out = torch.empty_like(q)
     for _ in range(10):
         k, v = k0.clone(), v0.clone()           # fresh replica: cold in L2 and MALL
         torch.cuda.synchronize()
-        pa.kv_write_fused(k, v, kn, vn, pos, bt, seq)
-        pa.decode(q, k, v, bt, sl, case.max_seq_len, case.scale, workspace=ws, out=out)
+        pa.decode_append(q, k, v, bt, sl, case.max_seq_len, case.scale, kn, vn, workspace=ws,
+                         out=out)
         torch.cuda.synchronize()
     src = torch.empty(256 << 20, dtype=torch.uint8, device=D.dev).fill_(1)
     dst = torch.empty_like(src)
@@ -316,6 +325,8 @@ def main():
                                                          rotate=False)
         extra["decode_ctx8192_b832_graph"] = bench_decode(D, pa, head_case, args.steps,
                                                           args.warmup, rotate=True, graph=True)
+        extra["decode_ctx8192_b832_separate_write"] = bench_decode(
+            D, pa, head_case, args.steps, args.warmup, rotate=True, separate=True)
         for B in (784, 832, 1024):
             print(f"[bench] decode_ctx32768_b{B}", file=sys.stderr, flush=True)
             extra[f"decode_ctx32768_b{B}"] = bench_decode(D, pa, W.decode_32k(B), args.steps,
@@ -349,13 +360,14 @@ def main():
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) bf16 K/V/q, random block tables)",
         "config": {"workload": "decode_ctx8192_b832: 1 seq, 8192 cached tokens + 1 written at "
-                               "position 8192 (slot-mapping KV write + split-K decode), page 832, "
+                               "position 8192 (slot-mapping KV write inside the split-K decode "
+                               "launch), page 832, "
                                "pool 64 pages, 24 q / 4 KV heads, head_dim 256",
                    "kv_bytes_per_step": head["kv_bytes"], "pool_replicas": head["replicas"]},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 3), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(),
-                     "kernel": "pa_decode (decode_split_kernel + decode_merge_kernel)",
+                     "kernel": "pa_decode_append (decode_split_kernel + decode_merge_kernel)",
                      "launch_ms_avg": round(head["kernel_ms_avg"], 6),
                      "algorithmic_bytes_per_launch": head["kv_bytes"]},
         "cpu_baseline": cpu,

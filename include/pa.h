@@ -157,6 +157,33 @@ int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
               size_t workspace_bytes, void* stream);
 
 /*
+ * One decode step with the new token's KV write in the same launch: for
+ * each sequence s with seq_lens[s] >= 1, the token at position
+ * pos = seq_lens[s] - 1 is appended and attended.  Equivalent to
+ *   pa_kv_write_fused(positions[s] = seq_lens[s] - 1, token_seq[s] = s, ...)
+ * followed by pa_decode(...) on the same stream, with identical output bits
+ * and identical cache contents afterwards ([PREP] §2: the new token's slot
+ * is its KV-cache write position; [ALIGN] §7 for the attention).
+ *
+ * k_cache, v_cache  modified in place: row pos % block_size of page
+ *                   block_table[s][pos / block_size] receives k_new[s] /
+ *                   v_new[s].  That page must be a valid page (it is read
+ *                   by the decode as well); sequences of length 0 write
+ *                   nothing.
+ * k_new, v_new      bf16 [num_seqs][num_kv_heads][256], 16-byte aligned.
+ * slot_out          int64 [num_seqs] or NULL: the slot of each appended
+ *                   token (not written for sequences of length 0).
+ * Other arguments, the workspace and errors: as pa_decode.
+ */
+int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16_t* v_cache,
+                     int64_t page_stride, const int32_t* block_table, int32_t bt_stride,
+                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                     int32_t block_size, float scale, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* k_new,
+                     const uint16_t* v_new, int64_t* slot_out, void* workspace,
+                     size_t workspace_bytes, void* stream);
+
+/*
  * Attention for one chunk of a chunked prefill of a single sequence
  * ([ALIGN] §6: q_len query tokens at positions start_pos .. start_pos +
  * q_len - 1, with the paged KV of the first start_pos + q_len tokens,

@@ -11,7 +11,7 @@ imports without it.
 """
 import importlib
 
-_API = ("LIB_PATH", "PAError", "build_info", "decode", "decode_workspace",
+_API = ("LIB_PATH", "PAError", "build_info", "decode", "decode_append", "decode_workspace",
         "decode_workspace_size", "kv_write", "kv_write_fused", "lib", "prefill_chunk",
         "slot_mapping", "strerror")
 

@@ -24,10 +24,12 @@ lib.pa_kv_write_fused.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _
 lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
                           _i32, _i32, _i32, _vp, _sz, _vp]
+lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32,
+                                 _f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
                                  _f32, _i32, _i32, _i32, _vp]
 for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
-           "pa_decode", "pa_prefill_chunk"):
+           "pa_decode", "pa_decode_append", "pa_prefill_chunk"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.pa_strerror.argtypes = [ctypes.c_int]
 lib.pa_strerror.restype = ctypes.c_char_p
@@ -193,6 +195,43 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale: 
                          bt.shape[1], _ptr(seq_lens), S, int(max_seq_len), B, float(scale),
                          GQA * H, H, HEAD_DIM, _ptr(workspace), workspace.numel(), _stream(q)),
            "pa_decode")
+    return out
+
+
+def decode_append(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale: float,
+                  k_new, v_new, workspace: torch.Tensor = None, out: torch.Tensor = None,
+                  slot_out: torch.Tensor = None) -> torch.Tensor:
+    """One decode step that first appends k_new/v_new [S, Hkv, 256] at position
+    seq_lens[s] - 1 of each sequence (same launch), then attends as decode()."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(q, "q", _BF16, k_cache.device)
+    S = q.shape[0]
+    for t, n in ((k_new, "k_new"), (v_new, "v_new")):
+        _need(t, n, _BF16, k_cache.device)
+        if t.shape != (S, H, HEAD_DIM):
+            raise ValueError(f"{n} must be [num_seqs, num_kv_heads, 256]")
+    _need(block_table, "block_table", (torch.int32,), k_cache.device)
+    _need(seq_lens, "seq_lens", (torch.int32,), k_cache.device)
+    if q.shape != (S, GQA * H, HEAD_DIM):
+        raise ValueError("q must be [num_seqs, 6 * num_kv_heads, 256]")
+    bt = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    if bt.shape[0] < S or seq_lens.numel() < S:
+        raise ValueError("block_table / seq_lens have fewer rows than q")
+    if slot_out is not None:
+        _need(slot_out, "slot_out", (torch.int64,), k_cache.device)
+        if slot_out.numel() < S:
+            raise ValueError("slot_out has fewer entries than q has sequences")
+    if workspace is None:
+        workspace = decode_workspace(S, max_seq_len, B, H, device=q.device)
+    _need(workspace, "workspace", (torch.uint8,), k_cache.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, k_cache.device)
+    _check(lib.pa_decode_append(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), stride,
+                                _ptr(bt), bt.shape[1], _ptr(seq_lens), S, int(max_seq_len), B,
+                                float(scale), GQA * H, H, HEAD_DIM, _ptr(k_new), _ptr(v_new),
+                                _ptr(slot_out), _ptr(workspace), workspace.numel(), _stream(q)),
+           "pa_decode_append")
     return out
 
 

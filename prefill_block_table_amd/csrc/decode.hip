@@ -31,10 +31,12 @@
 //    Each (item, workgroup) pair that shares work leaves one partial (m, l,
 //    unnormalised O) per KV head; an item done by a single workgroup writes
 //    bf16 output directly.
-// 2. decode_merge_kernel.  One workgroup per (sequence, query head, 16-dim
-//    slice); its 256 threads take 16 partials at a time, so all loads of a
-//    workgroup are in flight together.  Merge order is fixed: results are
-//    bitwise repeatable, no atomics anywhere.
+// 2. decode_merge_kernel.  One workgroup per (sequence, query head, 32-dim
+//    slice: one 128-byte line of a partial); its 256 threads load all (at
+//    most 256) partials of the slice in one round, so every load of a
+//    workgroup is in flight at once, then combine them with cross-lane
+//    shuffles.  Merge order is fixed: results are bitwise repeatable, no
+//    atomics anywhere.
 // Nothing is read past a page's or a sequence's last live row (such rows are
 // replaced by the page's first row, whose weight is exactly 0), so poisoned
 // rows never reach the output.
@@ -46,8 +48,8 @@
 namespace pa {
 
 const char* const kDecodeVariant =
-    "decode-v6(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-lds-dma,2stage,"
-    "mfma16x16x32-qk,tr16-vt,mfma16x16x16-pv,lazy-rescale)";
+    "decode-v7(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-lds-dma,2stage,"
+    "mfma16x16x32-qk,tr16-vt,mfma16x16x16-pv,lazy-rescale,append)";
 
 namespace {
 
@@ -58,8 +60,10 @@ constexpr int kTileBytes = 16 * kRowBytes;         // 16 K (or V) rows of one wa
 constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
 constexpr int kSmemBytes = kWaves * kStages * kStageBytes;   // 128 KB
 constexpr float kRescaleSlack = 8.f;               // log2 headroom before re-basing O
-constexpr int kMergeSlices = 16;                   // partials merged in parallel per dim
-constexpr int kMergeDims = 16;                     // dims per merge workgroup
+constexpr int kMergeSlices = 32;                   // partials merged in parallel per dim
+constexpr int kMergeDims = 32;                     // dims per merge workgroup (one 128 B line)
+constexpr int kMergeParts = 8;                     // partials per merge thread
+static_assert(kDecodeWorkgroups <= kMergeSlices * kMergeParts, "one merge round covers all partials");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define PA_LDS __attribute__((address_space(3)))
@@ -91,6 +95,14 @@ struct DecodeArgs {
   float* p_acc;            // [slot][heads_per_wg][6][256], slot = item + workgroup
   float* p_ml;             // [slot][heads_per_wg][6][2]
   int32_t* meta;           // [item][2]: first workgroup, number of partials
+  // Appended token (NULL k_new: plain decode).  Row [s][g] of k_new / v_new
+  // is the token at position seq_lens[s] - 1; it is stored to that slot of
+  // k_dst / v_dst (the same caches) and attended from the new rows.
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_dst;
+  uint16_t* v_dst;
+  int64_t* slot_out;       // [num_seqs] or NULL
 };
 
 __device__ __forceinline__ int clamp_len(int L, int max_len) {
@@ -106,11 +118,12 @@ __device__ __forceinline__ int live_steps(int L, int B, int spp, int step_tokens
 }
 
 // Workgroup ranges: workgroup w owns flattened steps [bnd(w), bnd(w + 1)),
-// bnd(w) = floor(w * T / N); the workgroup owning step x is
-// floor(((x + 1) * N - 1) / T).
-__device__ __forceinline__ int64_t wg_bound(int64_t w, int64_t T, int64_t N) { return w * T / N; }
-__device__ __forceinline__ int64_t wg_of(int64_t x, int64_t T, int64_t N) {
-  return ((x + 1) * N - 1) / T;
+// bnd(w) = floor(w * T / N).  With T = q N + r, bnd(w) = w q + floor(w r / N);
+// w, r <= N <= 256 and T < 2^31 (checked on the host), so this is 32-bit
+// arithmetic.  The workgroup owning step x is floor(((x + 1) N - 1) / T).
+__device__ __forceinline__ int wg_bound(int w, int q, int r, int N) { return w * q + (w * r) / N; }
+__device__ __forceinline__ int wg_of(int x, int T, int N) {
+  return (int)(((int64_t)(x + 1) * N - 1) / T);
 }
 
 // Pair reductions across lanes l and l ^ 16 (or l ^ 32) with the gfx950
@@ -159,130 +172,263 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 #define PA_DS_READ_TR16(dst, addr, off) \
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:" #off : "=v"(dst) : "v"(addr))
 
-// Sum over 256 threads (all threads get the result).
-__device__ __forceinline__ int64_t block_sum(int64_t v, int64_t* red) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
-  __syncthreads();
-  return red[0] + red[1] + red[2] + red[3];
-}
-
+template <int HPW>
 __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
+  constexpr int KSL = kWaves / HPW;      // waves sharing one KV head
+  constexpr int STOK = 16 * KSL;         // tokens per step
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
-  __shared__ int64_t red[4];
-  __shared__ int64_t scan_lds[kWaves];
+  __shared__ int red[2];
+  __shared__ int scan_lds[2][kWaves];
+  __shared__ int excl_lds[256];
+  __shared__ int lens_lds[256];
 
   const int wgi = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // wave index: uniform per wave, so head / slice indices and the cache page
+  // bases derived from them live in scalar registers
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int Hkv = a.num_kv_heads;
   const int Hq = Hkv * kGqa;
   const int B = a.block_size;
-  const int hpw = a.heads_per_wg;
-  const int ng = Hkv / hpw;               // items per sequence
-  const int ksl = kWaves / hpw;
-  const int jw = w % hpw;                 // this wave's KV head within the item
-  const int ks = w / hpw;                 // this wave's 16-token slice of a step
+  const int ng = Hkv / HPW;               // items per sequence
+  const int jw = w % HPW;                 // this wave's KV head within the item
+  const int ks = w / HPW;                 // this wave's 16-token slice of a step
   const int spp = a.steps_per_page;
-  const int stok = a.step_tokens;
   const int c16 = lane & 15;
   const int kq = lane >> 4;
 
   // Total steps T of the batch, this workgroup's range [x0, x1) and the
-  // sequence holding step x0.  One pass over seq_lens when the batch has at
-  // most 256 sequences (a second pass locates x0 in larger batches).
-  int64_t T = 0;
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
-    const int s = c0 + tid;
-    const int64_t v = s < a.num_seqs
-        ? (int64_t)live_steps(clamp_len(a.seq_lens[s], a.max_seq_len), B, spp, stok) * ng : 0;
-    T += block_sum(v, red);
+  // sequence holding step x0.  One sequence: one scalar load.  Otherwise one
+  // read of seq_lens (thread t takes sequences t, t + 256, ...) and a block
+  // scan give every sequence's first step; the lengths of the first 256
+  // sequences stay in LDS for the item loop.
+  int T = 0;
+  int s_cur = 0;
+  int seq_start = 0;    // flattened index of the first step of s_cur
+  const bool single = a.num_seqs == 1;
+  int L_single = 0;
+  if (single) {
+    L_single = clamp_len(load_const_i32(a.seq_lens), a.max_seq_len);
+    T = live_steps(L_single, B, spp, STOK) * ng;
+  } else {
+    for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
+      const int s = c0 + tid;
+      const int L = s < a.num_seqs ? clamp_len(a.seq_lens[s], a.max_seq_len) : 0;
+      if (c0 == 0) lens_lds[tid] = L;
+      const int v = live_steps(L, B, spp, STOK) * ng;
+      int incl = v;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
+      if (lane == 63) scan_lds[(c0 >> 8) & 1][w] = incl;
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        const int t = scan_lds[(c0 >> 8) & 1][ww];
+        before += ww < w ? t : 0;
+        total += t;
+      }
+      excl_lds[tid] = T + before + incl - v;    // first step of sequence s
+      T += total;
+      if (c0 + 256 < a.num_seqs) __syncthreads();
+    }
   }
   if (T == 0) return;
   // Effective workgroup count min(launched, T): every workgroup below it owns
   // at least one step, so the workgroups sharing an item are consecutive and
   // its partials occupy consecutive slots.
-  const int64_t N = T < a.num_wgs ? T : a.num_wgs;
+  const int N = T < a.num_wgs ? T : a.num_wgs;
   if (wgi >= N) return;
-  const int64_t x0 = wg_bound(wgi, T, N);
-  const int64_t x1 = wg_bound(wgi + 1, T, N);
+  const int tq = T / N, tr = T - tq * N;
+  const int x0 = wg_bound(wgi, tq, tr, N);
+  const int x1 = wg_bound(wgi + 1, tq, tr, N);
   if (x0 >= x1) return;
-  int s_cur = 0;
-  int64_t seq_start = 0;    // flattened index of the first step of s_cur
-  for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
-    const int s = c0 + tid;
-    const int64_t v = s < a.num_seqs
-        ? (int64_t)live_steps(clamp_len(a.seq_lens[s], a.max_seq_len), B, spp, stok) * ng : 0;
-    // exclusive prefix of v over the block: wave scan, then wave totals
-    int64_t incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const int64_t t = __shfl_up(incl, off);
-      if (lane >= off) incl += t;
-    }
+  if (single) {
+    // s_cur = 0, seq_start = 0
+  } else if (a.num_seqs <= 256) {
+    // sequence s holds x0 iff excl[s] <= x0 < excl[s] + steps(s) (exactly
+    // one s: empty sequences have empty ranges)
     __syncthreads();
-    if (lane == 63) scan_lds[w] = incl;
+    const int s = tid;
+    const int lo = excl_lds[s];
+    const int hi = lo + live_steps(lens_lds[s], B, spp, STOK) * ng;
+    if (s < a.num_seqs && lo <= x0 && x0 < hi) { red[0] = s; red[1] = lo; }
     __syncthreads();
-    int64_t before = 0, total = 0;
+    s_cur = __builtin_amdgcn_readfirstlane(red[0]);
+    seq_start = __builtin_amdgcn_readfirstlane(red[1]);
+  } else {
+    // larger batches: a second pass locates x0
+    for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
+      const int s = c0 + tid;
+      const int v = s < a.num_seqs
+          ? live_steps(clamp_len(a.seq_lens[s], a.max_seq_len), B, spp, STOK) * ng : 0;
+      int incl = v;
 #pragma unroll
-    for (int ww = 0; ww < kWaves; ++ww) {
-      before += ww < w ? scan_lds[ww] : 0;
-      total += scan_lds[ww];
-    }
-    const int64_t lo = seq_start + before + incl - v;
-    const int64_t hi = seq_start + before + incl;
-    const bool found = x0 < seq_start + total;
-    if (found) {
-      if (s < a.num_seqs && lo <= x0 && x0 < hi) { red[0] = s; red[1] = lo; }
+      for (int off = 1; off < 64; off <<= 1) {
+        const int t = __shfl_up(incl, off);
+        if (lane >= off) incl += t;
+      }
       __syncthreads();
-      // wave-uniform from here on (scalar registers, scalar block-table loads)
-      s_cur = __builtin_amdgcn_readfirstlane((int)red[0]);
-      seq_start = ((int64_t)__builtin_amdgcn_readfirstlane((int)(red[1] >> 32)) << 32) |
-                  (uint32_t)__builtin_amdgcn_readfirstlane((int)(red[1] & 0xffffffff));
-      break;
+      if (lane == 63) scan_lds[0][w] = incl;
+      __syncthreads();
+      int before = 0, total = 0;
+#pragma unroll
+      for (int ww = 0; ww < kWaves; ++ww) {
+        before += ww < w ? scan_lds[0][ww] : 0;
+        total += scan_lds[0][ww];
+      }
+      const int lo = seq_start + before + incl - v;
+      const int hi = seq_start + before + incl;
+      const bool found = x0 < seq_start + total;
+      if (found) {
+        if (s < a.num_seqs && lo <= x0 && x0 < hi) { red[0] = s; red[1] = lo; }
+        __syncthreads();
+        s_cur = __builtin_amdgcn_readfirstlane(red[0]);
+        seq_start = __builtin_amdgcn_readfirstlane(red[1]);
+        break;
+      }
+      seq_start += total;
     }
-    seq_start += total;
   }
 
-  const int64_t row_stride = (int64_t)Hkv * kHeadDim;   // elements per cache row (token)
-  char* vbase = smem + w * (kStages * kStageBytes);
+  // ---- per-lane constants, computed once ----
+  const uint32_t rs_bytes = (uint32_t)Hkv * kRowBytes;   // bytes per cache row (token)
+  const int64_t page_bytes = a.page_stride * 2;
+  // Direct-to-LDS load j of a step moves rows 2j (lanes 0..31) and 2j + 1
+  // (lanes 32..63) of this wave's 16; lane offset from the step's first row.
+  // K rows: 16-byte chunk c of row r lands at position c ^ (r & 7); V rows at
+  // c ^ ((r & 3) << 1) (bank-conflict-free operand reads, see compute).
+  const int pos = lane & 31;
+  const int half = lane >> 5;
+  uint32_t koff[8], voff[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int row = 2 * j + half;
+    koff[j] = (uint32_t)row * rs_bytes + ((uint32_t)(pos ^ kswz(row)) << 4);
+    voff[j] = (uint32_t)row * rs_bytes + ((uint32_t)(pos ^ vswz(row)) << 4);
+  }
+  char* stA = smem + w * (kStages * kStageBytes);
+  char* stB = stA + kStageBytes;
+  // Operand read addresses in stage A (stage B: + kStageBytes).
+  // K A-operand: row c16 (key), 16-byte chunk 4*t + kq at position
+  // (4*t + kq) ^ (c16 & 7) = 8*(t >> 1) + (4*((t & 1) ^ (c16 >> 2 & 1)) + (kq ^ (c16 & 3))).
+  const uint32_t kr = lds_addr(stA) + c16 * kRowBytes;
+  const uint32_t k_even = kr + ((((c16 >> 2) & 1) * 4 + (kq ^ (c16 & 3))) << 4);
+  const uint32_t k_odd = kr + (((((c16 >> 2) & 1) ^ 1) * 4 + (kq ^ (c16 & 3))) << 4);
+  // V^T operands.  Transposing read: lane (kq, c16) points at
+  // V[4*kq + c16/4][16*db + 4*(c16%4)] and receives V[4*kq + e][16*db + c16],
+  // e = 0..3: the A operand of V^T.  With the row swizzle the byte offset
+  // is 32*((db & 3) ^ (vrow & 3)) + 128*(db >> 2) + 16*h1 + 8*h0.
+  const int vrow = 4 * kq + (c16 >> 2);
+  const uint32_t vr = lds_addr(stA) + kTileBytes + vrow * kRowBytes + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
+  const uint32_t v0 = vr + ((0 ^ (vrow & 3)) << 5);
+  const uint32_t v1 = vr + ((1 ^ (vrow & 3)) << 5);
+  const uint32_t v2 = vr + ((2 ^ (vrow & 3)) << 5);
+  const uint32_t v3 = vr + ((3 ^ (vrow & 3)) << 5);
+  // Query head of this lane's S^T column: lanes 6..15 of each 16 repeat
+  // heads 0..3 / 0..5 (valid data, results discarded), so no lane is masked.
+  const int qh = c16 % kGqa;
 
   // Walk the items (s, hg) overlapping [x0, x1).
-  int64_t x = x0;
+  int x = x0;
   while (x < x1) {
     const int s = __builtin_amdgcn_readfirstlane(s_cur);
-    const int L = clamp_len(a.seq_lens[s], a.max_seq_len);
-    const int steps = live_steps(L, B, spp, stok);
+    const int L = single ? L_single : __builtin_amdgcn_readfirstlane(
+        s < 256 ? lens_lds[s] : clamp_len(a.seq_lens[s], a.max_seq_len));
+    const int steps = live_steps(L, B, spp, STOK);
     if (steps == 0) { ++s_cur; continue; }
-    const int hg = (int)((x - seq_start) / steps);
-    const int64_t item_start = seq_start + (int64_t)hg * steps;
-    const int64_t item_end = item_start + steps;
-    const int la = (int)(x - item_start);
-    const int lb = (int)((x1 < item_end ? x1 : item_end) - item_start);
+    const int hg = ng == 1 ? 0 : (x - seq_start) / steps;
+    const int item_start = seq_start + hg * steps;
+    const int item_end = item_start + steps;
+    const int la = x - item_start;
+    const int lb = (x1 < item_end ? x1 : item_end) - item_start;
     const int item = s * ng + hg;
-    const int g = hg * hpw + jw;
-    const int64_t first_wg = wg_of(item_start, T, N);
-    const int64_t last_wg = wg_of(item_end - 1, T, N);
-    const int nparts = (int)(last_wg - first_wg + 1);
-
+    const int g = hg * HPW + jw;
     const int32_t* bt = a.block_table + (int64_t)s * a.bt_stride;
+    const int last_page = (L - 1) / B;
+    const char* kcache = reinterpret_cast<const char*>(a.k_cache + (int64_t)g * kHeadDim);
+    const char* vcache = reinterpret_cast<const char*>(a.v_cache + (int64_t)g * kHeadDim);
+    // Appending (pa_decode_append): the step holding the new token takes its
+    // K/V rows straight from k_new / v_new (see issue); the workgroup that
+    // owns the item's last step also stores them to the cache (after its
+    // loop).  Nothing else in the launch reads that cache row.
+    const bool append = a.k_new != nullptr;
+    const char* knew = append ? reinterpret_cast<const char*>(a.k_new + ((int64_t)s * Hkv + g) * kHeadDim) : nullptr;
+    const char* vnew = append ? reinterpret_cast<const char*>(a.v_new + ((int64_t)s * Hkv + g) * kHeadDim) : nullptr;
+    const bool append_store = append && lb == steps && ks == 0;
+
     // Q^T as the B operand of S^T = K Q^T (16x16x32): lane supplies column
-    // n = c16 (query head; columns 6..15 are zero) and k = 8*kq + i of
-    // operand step t, mapped to d = 32*t + 8*kq + i (K's A operand uses the
-    // same map).
+    // n = c16 and k = 8*kq + i of operand step t, mapped to d = 32*t + 8*kq + i
+    // (K's A operand uses the same map).
     bf16x8 qb[8];
     {
-      const uint16_t* qp = a.q + ((int64_t)s * Hq + g * kGqa + (c16 < kGqa ? c16 : 0)) * kHeadDim + 8 * kq;
+      const uint16_t* qp = a.q + ((int64_t)s * Hq + g * kGqa + qh) * kHeadDim + 8 * kq;
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (c16 < kGqa) v = load16(qp + 32 * t);
-        qb[t] = as_bf16x8(v);
-      }
+      for (int t = 0; t < 8; ++t) qb[t] = as_bf16x8(load16(qp + 32 * t));
     }
+    u32x2 knew_v = {0u, 0u}, vnew_v = {0u, 0u};
+    if (append_store) {
+      knew_v = *reinterpret_cast<const u32x2*>(knew + 8 * lane);
+      vnew_v = *reinterpret_cast<const u32x2*>(vnew + 8 * lane);
+    }
+
+    // Issue cursor: logical page ip and step isp inside it; the block-table
+    // entry is read (a scalar load) when a step of a new page is issued.
+    const int page0 = la / spp;
+    int ip = page0;
+    int isp = la - page0 * spp;
+    int ip_loaded = -1;
+    int64_t ip_base = 0;
+    auto issue = [&](char* st) {
+      if (ip != ip_loaded) {
+        ip_loaded = ip;
+        ip_base = (int64_t)load_const_i32(bt + ip) * page_bytes;
+      }
+      const int kb = isp * STOK + 16 * ks;          // first row of this wave's 16
+      const int page_len = min(B, L - ip * B);      // live rows of the page
+      // rows up to lim - 1 come from the cache as they are; the rest are
+      // masked rows (or, when appending, the new token's row and after)
+      const int lim = (append && ip == last_page) ? page_len - 1 : page_len;
+      if (kb + 16 <= lim) {
+        const char* kp = kcache + ip_base + (uint32_t)kb * rs_bytes;
+        const char* vp = vcache + ip_base + (uint32_t)kb * rs_bytes;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          __builtin_amdgcn_global_load_lds(kp + koff[j], (PA_LDS void*)(st + j * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(vp + voff[j], (PA_LDS void*)(st + kTileBytes + j * 1024), 16, 0, 0);
+        }
+      } else {
+        // Tail step: rows at or past lim reload the page's first row
+        // (finite; masked out of the softmax) or, when appending, take
+        // k_new / v_new.
+        const char* kp = kcache + ip_base;
+        const char* vp = vcache + ip_base;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int row = 2 * j + half;
+          const int key = kb + row;
+          const bool fresh = key >= lim && append && ip == last_page;
+          const uint32_t roff = (uint32_t)(key < lim ? key : 0) * rs_bytes;
+          const uint32_t kc = (uint32_t)(pos ^ kswz(row)) << 4;
+          const uint32_t vc = (uint32_t)(pos ^ vswz(row)) << 4;
+          __builtin_amdgcn_global_load_lds(fresh ? knew + kc : kp + (roff + kc),
+                                           (PA_LDS void*)(st + j * 1024), 16, 0, 0);
+          __builtin_amdgcn_global_load_lds(fresh ? vnew + vc : vp + (roff + vc),
+                                           (PA_LDS void*)(st + kTileBytes + j * 1024), 16, 0, 0);
+        }
+      }
+      if (++isp == spp) { isp = 0; ++ip; }
+    };
+    // The first two steps go out before the rest of the setup.  Vector
+    // memory operations retire in issue order: the q (and k_new) loads above
+    // are older than step la's.
+    issue(stA);
+    if (la + 1 < lb) issue(stB);
+
     // Softmax state of query head c16.  O^T and l are kept relative to the
     // reference m_run, which is re-based only when a score exceeds it by more
     // than kRescaleSlack (so weights stay <= 2^8); the final O / l is the same.
@@ -291,92 +437,39 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
     for (int db = 0; db < 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    const uint16_t* kbase_g = a.k_cache + (int64_t)g * kHeadDim;
-    const uint16_t* vbase_g = a.v_cache + (int64_t)g * kHeadDim;
-    // Row geometry of local step u: first row kb (of this wave's 16) and the
-    // page's live rows.
-    auto geom = [&](int u, int& kb, int& page_len) {
-      const int page = u / spp;
-      page_len = min(B, L - page * B);
-      kb = (u - page * spp) * stok + 16 * ks;
-      return page;
-    };
-    // Issue one step: 8 + 8 direct-to-LDS loads of two rows (1 KB) each.
-    // Rows past the page's live end reload the page's first row (finite;
-    // masked out of the softmax).
-    // Block-table entry of the page being loaded, re-read only when the
-    // page changes (a scalar load).
-    int cached_page = -1;
-    int64_t cached_poff = 0;
-    auto issue = [&](int u, char* st) {
-      int kb, page_len;
-      const int page = geom(u, kb, page_len);
-      if (page != cached_page) {
-        cached_page = page;
-        cached_poff = (int64_t)load_const_i32(bt + page) * a.page_stride;
-      }
-      // Wave-uniform page bases and 32-bit per-lane byte offsets (a page of
-      // one KV head's rows spans < 2^31 bytes).
-      const int64_t poff = cached_poff;
-      const char* kpage = reinterpret_cast<const char*>(kbase_g + poff);
-      const char* vpage = reinterpret_cast<const char*>(vbase_g + poff);
-      const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
-      const int pos = lane & 31;
-      const int half = lane >> 5;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int row = 2 * j + half;
-        const int key = kb + row;
-        const uint32_t roff = (uint32_t)(key < page_len ? key : 0) * rs_bytes;
-        __builtin_amdgcn_global_load_lds(kpage + roff + ((pos ^ kswz(row)) << 4),
-                                         (PA_LDS void*)(st + j * 1024), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vpage + roff + ((pos ^ vswz(row)) << 4),
-                                         (PA_LDS void*)(st + kTileBytes + j * 1024), 16, 0, 0);
-      }
-    };
-    auto compute = [&](int u, const char* st) {
-      int kb, page_len;
-      geom(u, kb, page_len);
+    // Compute cursor (same walk as the issue cursor, one or two steps behind).
+    int cp = page0;
+    int csp = la - page0 * spp;
+    auto compute = [&](const uint32_t soff) {
+      const int kb = csp * STOK + 16 * ks;
+      const int page_len = min(B, L - cp * B);
+      if (++csp == spp) { csp = 0; ++cp; }
       // Operand reads from LDS, written as inline asm: the compiler's wait
       // insertion cannot tell which direct-to-LDS load wrote which bytes and
       // would otherwise drain every in-flight load (the prefetched step too)
       // before each read.  The explicit vmcnt wait before compute() orders
       // these reads after this step's loads; one lgkmcnt wait below, which
       // takes every result as an operand, orders their uses after the reads.
-      const uint32_t st_lds = lds_addr(st);
-      // K A-operand: row c16 (key), 16-byte chunk 4*t + kq at position
-      // (4*t + kq) ^ (c16 & 7) = 8*(t >> 1) + (4*((t & 1) ^ (c16 >> 2 & 1)) + (kq ^ (c16 & 3))).
-      const uint32_t kr = st_lds + c16 * kRowBytes;
-      const uint32_t k_even = kr + ((((c16 >> 2) & 1) * 4 + (kq ^ (c16 & 3))) << 4);
-      const uint32_t k_odd = kr + (((((c16 >> 2) & 1) ^ 1) * 4 + (kq ^ (c16 & 3))) << 4);
+      const uint32_t ke = k_even + soff, ko = k_odd + soff;
+      const uint32_t w0 = v0 + soff, w1 = v1 + soff, w2 = v2 + soff, w3 = v3 + soff;
       u32x4 kv[8];
-      PA_DS_READ_B128(kv[0], k_even, 0);
-      PA_DS_READ_B128(kv[1], k_odd, 0);
-      PA_DS_READ_B128(kv[2], k_even, 128);
-      PA_DS_READ_B128(kv[3], k_odd, 128);
-      PA_DS_READ_B128(kv[4], k_even, 256);
-      PA_DS_READ_B128(kv[5], k_odd, 256);
-      PA_DS_READ_B128(kv[6], k_even, 384);
-      PA_DS_READ_B128(kv[7], k_odd, 384);
-      // V^T operands.  Transposing read: lane (kq, c16) points at
-      // V[4*kq + c16/4][16*db + 4*(c16%4)] and receives V[4*kq + e][16*db + c16],
-      // e = 0..3: the A operand of V^T.  With the row swizzle the byte offset
-      // is 32*((db & 3) ^ (vrow & 3)) + 128*(db >> 2) + 16*h1 + 8*h0.
-      const int vrow = 4 * kq + (c16 >> 2);
-      const uint32_t vr = st_lds + kTileBytes + vrow * kRowBytes + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
-      const uint32_t v0 = vr + ((0 ^ (vrow & 3)) << 5);
-      const uint32_t v1 = vr + ((1 ^ (vrow & 3)) << 5);
-      const uint32_t v2 = vr + ((2 ^ (vrow & 3)) << 5);
-      const uint32_t v3 = vr + ((3 ^ (vrow & 3)) << 5);
+      PA_DS_READ_B128(kv[0], ke, 0);
+      PA_DS_READ_B128(kv[1], ko, 0);
+      PA_DS_READ_B128(kv[2], ke, 128);
+      PA_DS_READ_B128(kv[3], ko, 128);
+      PA_DS_READ_B128(kv[4], ke, 256);
+      PA_DS_READ_B128(kv[5], ko, 256);
+      PA_DS_READ_B128(kv[6], ke, 384);
+      PA_DS_READ_B128(kv[7], ko, 384);
       u32x2 va[16];
-      PA_DS_READ_TR16(va[0], v0, 0);    PA_DS_READ_TR16(va[1], v1, 0);
-      PA_DS_READ_TR16(va[2], v2, 0);    PA_DS_READ_TR16(va[3], v3, 0);
-      PA_DS_READ_TR16(va[4], v0, 128);  PA_DS_READ_TR16(va[5], v1, 128);
-      PA_DS_READ_TR16(va[6], v2, 128);  PA_DS_READ_TR16(va[7], v3, 128);
-      PA_DS_READ_TR16(va[8], v0, 256);  PA_DS_READ_TR16(va[9], v1, 256);
-      PA_DS_READ_TR16(va[10], v2, 256); PA_DS_READ_TR16(va[11], v3, 256);
-      PA_DS_READ_TR16(va[12], v0, 384); PA_DS_READ_TR16(va[13], v1, 384);
-      PA_DS_READ_TR16(va[14], v2, 384); PA_DS_READ_TR16(va[15], v3, 384);
+      PA_DS_READ_TR16(va[0], w0, 0);    PA_DS_READ_TR16(va[1], w1, 0);
+      PA_DS_READ_TR16(va[2], w2, 0);    PA_DS_READ_TR16(va[3], w3, 0);
+      PA_DS_READ_TR16(va[4], w0, 128);  PA_DS_READ_TR16(va[5], w1, 128);
+      PA_DS_READ_TR16(va[6], w2, 128);  PA_DS_READ_TR16(va[7], w3, 128);
+      PA_DS_READ_TR16(va[8], w0, 256);  PA_DS_READ_TR16(va[9], w1, 256);
+      PA_DS_READ_TR16(va[10], w2, 256); PA_DS_READ_TR16(va[11], w3, 256);
+      PA_DS_READ_TR16(va[12], w0, 384); PA_DS_READ_TR16(va[13], w1, 384);
+      PA_DS_READ_TR16(va[14], w2, 384); PA_DS_READ_TR16(va[15], w3, 384);
       asm volatile("s_waitcnt lgkmcnt(0)"
                    : "+v"(kv[0]), "+v"(kv[1]), "+v"(kv[2]), "+v"(kv[3]), "+v"(kv[4]), "+v"(kv[5]),
                      "+v"(kv[6]), "+v"(kv[7]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]),
@@ -390,11 +483,16 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[t]), qb[t], s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kv[t + 4]), qb[t + 4], s1, 0, 0, 0);
       }
-      // lane: query head c16, keys kb + 4*kq + q4
+      // lane: query head c16, keys kb + 4*kq + q4; rows past the page's live
+      // end (only in a page's last step) are masked
       float sv[4];
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4)
-        sv[q4] = (kb + 4 * kq + q4 < page_len) ? (s0[q4] + s1[q4]) * a.scale_log2 : -INFINITY;
+      for (int q4 = 0; q4 < 4; ++q4) sv[q4] = (s0[q4] + s1[q4]) * a.scale_log2;
+      if (kb + 16 > page_len) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          if (kb + 4 * kq + q4 >= page_len) sv[q4] = -INFINITY;
+      }
       const float mx = pair32_max(pair16_max(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3]))));
       if (__any(mx > m_run + kRescaleSlack)) {
         const float m_new = fmaxf(m_run, mx);
@@ -415,31 +513,43 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, va[db]), pb, o[db], 0, 0, 0);
     };
 
-    // Two-stage pipeline, unrolled by two so stage addresses are static.
-    char* stA = vbase;
-    char* stB = vbase + kStageBytes;
-    issue(la, stA);
+    // Two-stage pipeline.  Entering iteration u, steps u and (if it exists)
+    // u + 1 are in flight.
     for (int u = la; u < lb; u += 2) {
       if (u + 1 < lb) {
-        issue(u + 1, stB);
         PA_WAIT_VMCNT(16);   // step u has landed; step u + 1 may be in flight
       } else {
         PA_WAIT_VMCNT(0);
       }
-      compute(u, stA);
-        if (u + 1 >= lb) break;
+      compute(0);
+      if (u + 1 >= lb) break;
       if (u + 2 < lb) {
-        issue(u + 2, stA);
+        issue(stA);
         PA_WAIT_VMCNT(16);
       } else {
         PA_WAIT_VMCNT(0);
       }
-      compute(u + 1, stB);
+      compute(kStageBytes);
+      if (u + 3 < lb) issue(stB);
     }
+    if (append_store) {
+      const int64_t page_id = load_const_i32(bt + last_page);
+      const int64_t off = (int64_t)(L - 1) - (int64_t)last_page * B;
+      const int64_t dst = page_id * a.page_stride + off * Hkv * kHeadDim + (int64_t)g * kHeadDim + 4 * lane;
+      *reinterpret_cast<u32x2*>(a.k_dst + dst) = knew_v;
+      *reinterpret_cast<u32x2*>(a.v_dst + dst) = vnew_v;
+      if (a.slot_out && jw == 0 && lane == 0) a.slot_out[s] = page_id * B + off;
+    }
+    // Partial slots of this item: its workgroups are consecutive; only the
+    // workgroup's first item can have started in an earlier workgroup and
+    // only its last can continue in a later one.
+    const int first_wg = item_start >= x0 ? wgi : (item_start == 0 ? 0 : wg_of(item_start, T, N));
+    const int last_wg = item_end <= x1 ? wgi : (item_end == T ? N - 1 : wg_of(item_end - 1, T, N));
+    const int nparts = last_wg - first_wg + 1;
 
     // With fewer than 4 KV heads per item, waves of one head merge through
     // LDS (the stages are free now).
-    if (ksl > 1) {
+    if (KSL > 1) {
       __syncthreads();
       float* macc = reinterpret_cast<float*>(smem);                 // [4][6][256]
       float* mml = macc + kWaves * kGqa * kHeadDim;                 // [4][6][2]
@@ -452,13 +562,15 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
       __syncthreads();
       if (ks == 0 && c16 < kGqa) {
         float M = -INFINITY;
-        for (int k2_ = 0; k2_ < ksl; ++k2_) M = fmaxf(M, mml[((w + k2_ * hpw) * kGqa + c16) * 2]);
+#pragma unroll
+        for (int k2 = 0; k2 < KSL; ++k2) M = fmaxf(M, mml[((w + k2 * HPW) * kGqa + c16) * 2]);
         const float mu = M == -INFINITY ? 0.f : M;
         float Ls = 0.f;
 #pragma unroll
         for (int db = 0; db < 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int k2_ = 0; k2_ < ksl; ++k2_) {
-          const int ww = w + k2_ * hpw;
+#pragma unroll
+        for (int k2 = 0; k2 < KSL; ++k2) {
+          const int ww = w + k2 * HPW;
           const float f = fast_exp2(mml[(ww * kGqa + c16) * 2] - mu);
           Ls += f * mml[(ww * kGqa + c16) * 2 + 1];
 #pragma unroll
@@ -482,17 +594,17 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
         }
       } else {
         const int64_t slot = (int64_t)item + wgi;
-        float* pacc = a.p_acc + (slot * hpw + jw) * (kGqa * kHeadDim) + c16 * kHeadDim + 4 * kq;
+        float* pacc = a.p_acc + (slot * HPW + jw) * (kGqa * kHeadDim) + c16 * kHeadDim + 4 * kq;
 #pragma unroll
         for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(pacc + 16 * db) = o[db];
         if (kq == 0) {
-          a.p_ml[(slot * hpw + jw) * (kGqa * 2) + 2 * c16] = m_run;
-          a.p_ml[(slot * hpw + jw) * (kGqa * 2) + 2 * c16 + 1] = l_run;
+          a.p_ml[(slot * HPW + jw) * (kGqa * 2) + 2 * c16] = m_run;
+          a.p_ml[(slot * HPW + jw) * (kGqa * 2) + 2 * c16 + 1] = l_run;
         }
       }
     }
     if (tid == 0 && first_wg == wgi) {
-      a.meta[2 * item] = (int32_t)first_wg;
+      a.meta[2 * item] = first_wg;
       a.meta[2 * item + 1] = nparts;
     }
     x = item_start + lb;
@@ -500,19 +612,21 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the partials: workgroup (query head h, 16-dim slice, sequence).
-// Thread t: slice z = t / 16 takes partials z, z + 16, ...; dim d = t % 16.
+// Merge of the partials: workgroup (query head h, 32-dim slice, sequence).
+// Thread t: slice z = t / 8 takes partials z, z + 32, ..., z + 224; it reads
+// dims 4*(t % 8) .. +3 of the slice, so eight threads read one partial's
+// 128-byte line of the slice.
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
-  __shared__ float red_o[kMergeSlices][kMergeDims];
-  __shared__ float red_m[kMergeSlices];
-  __shared__ float red_l[kMergeSlices];
+  __shared__ __attribute__((aligned(16))) float red_o[4][kMergeDims];
+  __shared__ float red_m[4];
+  __shared__ float red_l[4];
   const int h = blockIdx.x / (kHeadDim / kMergeDims);
   const int dc = blockIdx.x % (kHeadDim / kMergeDims);
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
-  const int z = tid / kMergeDims;
-  const int dd = tid % kMergeDims;
-  const int d = dc * kMergeDims + dd;
+  const int z = tid / (kMergeDims / 4);
+  const int dg = tid % (kMergeDims / 4);
+  const int d = dc * kMergeDims + 4 * dg;
   const int Hkv = a.num_kv_heads;
   const int hpw = a.heads_per_wg;
   const int g = h / kGqa;
@@ -520,64 +634,91 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   const int item = s * (Hkv / hpw) + g / hpw;
   const int jw = g % hpw;
   uint16_t* outp = a.out + ((int64_t)s * Hkv * kGqa + h) * kHeadDim + d;
+  // A workgroup leaves at most one partial per item and there are at most
+  // kDecodeWorkgroups of them, so one round of kMergeParts loads per thread
+  // covers every partial.  The partials of item i sit at slots
+  // i + first .. i + first + nparts - 1, where (first, nparts) come from the
+  // split kernel's meta; first is 0 for the batch's first item (every item of
+  // a single-sequence batch with <= 4 KV heads), so those loads are issued
+  // together with the meta load, assuming first = 0, and re-issued only when
+  // meta says otherwise.  Every slot below items + num_wgs is allocated, so
+  // the guessed loads stay in bounds.
+  constexpr int kParts = kMergeParts;
+  const int64_t pml = (int64_t)hpw * (kGqa * 2);          // stride between consecutive slots
+  const int64_t pacc = (int64_t)hpw * (kGqa * kHeadDim);
+  float mv[kParts], lv[kParts];
+  f32x4 av[kParts];
+  auto load_parts = [&](int64_t slot0, int count) {
+    const float* ml = a.p_ml + (slot0 * hpw + jw) * (kGqa * 2) + 2 * hh;
+    const float* acc = a.p_acc + (slot0 * hpw + jw) * (kGqa * kHeadDim) + hh * kHeadDim + d;
+#pragma unroll
+    for (int k = 0; k < kParts; ++k) {
+      const int p = z + k * kMergeSlices;
+      const bool ok = p < count;
+      mv[k] = ok ? ml[p * pml] : -INFINITY;
+      lv[k] = ok ? ml[p * pml + 1] : 0.f;
+      av[k] = ok ? *reinterpret_cast<const f32x4*>(acc + p * pacc) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  load_parts(item, a.num_wgs);
+  // meta of an empty sequence is stale and unused
+  const int first = a.meta[2 * item];
+  const int nparts = a.meta[2 * item + 1];
   const int L = clamp_len(a.seq_lens[s], a.max_seq_len);
   if (L == 0) {
-    if (z == 0) *outp = 0;
+    if (z == 0) *reinterpret_cast<u32x2*>(outp) = u32x2{0u, 0u};
     return;
   }
-  const int nparts = a.meta[2 * item + 1];
   if (nparts <= 1) return;                 // the split kernel wrote the output
-  const int64_t slot0 = (int64_t)item + a.meta[2 * item];
-  const float* ml = a.p_ml + (slot0 * hpw + jw) * (kGqa * 2) + 2 * hh;
-  const float* acc = a.p_acc + (slot0 * hpw + jw) * (kGqa * kHeadDim) + hh * kHeadDim + d;
-  const int64_t pstride = (int64_t)hpw;    // consecutive slots
-
-  // One pass: each slice keeps its own running max.
-  float M = -INFINITY, O = 0.f, Ls = 0.f;
-#ifndef PA_MERGE_UNROLL
-#define PA_MERGE_UNROLL 8
-#endif
-  constexpr int kUnroll = PA_MERGE_UNROLL;
-  for (int p0 = z; p0 < nparts; p0 += kMergeSlices * kUnroll) {
-    float mv[kUnroll], lv[kUnroll], av[kUnroll];
+  if (first != 0) load_parts((int64_t)item + first, nparts);
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const int p = p0 + k * kMergeSlices;
-      const bool ok = p < nparts;
-      mv[k] = ok ? ml[p * pstride * (kGqa * 2)] : -INFINITY;
-      lv[k] = ok ? ml[p * pstride * (kGqa * 2) + 1] : 0.f;
-      av[k] = ok ? acc[p * pstride * (kGqa * kHeadDim)] : 0.f;
-    }
-    float mb = M;
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) mb = fmaxf(mb, mv[k]);
-    const float mu = mb == -INFINITY ? 0.f : mb;
-    const float r = fast_exp2(M - mu);
-    O *= r;
-    Ls *= r;
-#pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      const float f = fast_exp2(mv[k] - mu);
-      Ls += f * lv[k];
-      O += f * av[k];
-    }
-    M = mb;
+  for (int k = 0; k < kParts; ++k) {
+    if (z + k * kMergeSlices >= nparts) { mv[k] = -INFINITY; lv[k] = 0.f; av[k] = f32x4{0.f, 0.f, 0.f, 0.f}; }
   }
-  red_o[z][dd] = O;
-  if (dd == 0) { red_m[z] = M; red_l[z] = Ls; }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kParts; ++k) M = fmaxf(M, mv[k]);
+  const float mu = M == -INFINITY ? 0.f : M;
+  float Ls = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < kParts; ++k) {
+    const float f = fast_exp2(mv[k] - mu);
+    Ls += f * lv[k];
+    O += f * av[k];
+  }
+  // Combine the 32 slices: within a wave over lane bits 3..5 (slices
+  // 8w' .. 8w'+7), then the four waves' results through LDS.
+  auto combine = [&](float M2, float L2, f32x4 O2) {
+    const float Mn = fmaxf(M, M2);
+    const float mu = Mn == -INFINITY ? 0.f : Mn;
+    const float f1 = fast_exp2(M - mu), f2 = fast_exp2(M2 - mu);
+    Ls = f1 * Ls + f2 * L2;
+    O = f1 * O + f2 * O2;
+    M = Mn;
+  };
+#pragma unroll
+  for (int off = 8; off < 64; off <<= 1) {
+    f32x4 O2;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) O2[r] = __shfl_xor(O[r], off);
+    const float M2 = __shfl_xor(M, off);
+    const float L2 = __shfl_xor(Ls, off);
+    combine(M2, L2, O2);
+  }
+  const int wv = tid >> 6;
+  if ((tid & 63) < kMergeDims / 4) {
+    *reinterpret_cast<f32x4*>(&red_o[wv][4 * dg]) = O;
+    if (dg == 0) { red_m[wv] = M; red_l[wv] = Ls; }
+  }
   __syncthreads();
-  if (z == 0) {
-    float Mt = -INFINITY;
+  if (tid < kMergeDims / 4) {
 #pragma unroll
-    for (int zz = 0; zz < kMergeSlices; ++zz) Mt = fmaxf(Mt, red_m[zz]);
-    float Ot = 0.f, Lt = 0.f;
-#pragma unroll
-    for (int zz = 0; zz < kMergeSlices; ++zz) {
-      const float f = fast_exp2(red_m[zz] - Mt);
-      Ot += f * red_o[zz][dd];
-      Lt += f * red_l[zz];
-    }
-    *outp = (uint16_t)f32_to_bf16_rne(Ot / Lt);
+    for (int ww = 1; ww < 4; ++ww)
+      combine(red_m[ww], red_l[ww], *reinterpret_cast<const f32x4*>(&red_o[ww][4 * dg]));
+    const float inv = 1.f / Ls;
+    *reinterpret_cast<u32x2*>(outp) = u32x2{pack_bf16x2(O[0] * inv, O[1] * inv),
+                                             pack_bf16x2(O[2] * inv, O[3] * inv)};
   }
 }
 
@@ -609,6 +750,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size
   int64_t n = kDecodeWorkgroups;
   if (n > steps_ub) n = steps_ub;
   p.num_wgs = (int32_t)n;
+  p.steps_ub = steps_ub;
   const size_t slots = (size_t)(items + n);
   size_t off = 0;
   p.meta_off = off;  off += align256((size_t)items * 2 * sizeof(int32_t));
@@ -623,7 +765,8 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          const int32_t* block_table, int32_t bt_stride,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                          int32_t block_size, float scale, int32_t num_kv_heads,
-                         const DecodePlan& plan, void* workspace, hipStream_t stream) {
+                         const DecodePlan& plan, void* workspace, const DecodeAppend* append,
+                         hipStream_t stream) {
   DecodeArgs a;
   char* ws = static_cast<char*>(workspace);
   a.out = out;
@@ -646,7 +789,16 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   a.meta = reinterpret_cast<int32_t*>(ws + plan.meta_off);
   a.p_ml = reinterpret_cast<float*>(ws + plan.p_ml_off);
   a.p_acc = reinterpret_cast<float*>(ws + plan.p_acc_off);
-  hipLaunchKernelGGL(decode_split_kernel, dim3(plan.num_wgs), dim3(256), 0, stream, a);
+  a.k_new = append ? append->k_new : nullptr;
+  a.v_new = append ? append->v_new : nullptr;
+  a.k_dst = append ? append->k_cache : nullptr;
+  a.v_dst = append ? append->v_cache : nullptr;
+  a.slot_out = append ? append->slot_out : nullptr;
+  switch (plan.heads_per_wg) {
+    case 4: hipLaunchKernelGGL(decode_split_kernel<4>, dim3(plan.num_wgs), dim3(256), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL(decode_split_kernel<2>, dim3(plan.num_wgs), dim3(256), 0, stream, a); break;
+    default: hipLaunchKernelGGL(decode_split_kernel<1>, dim3(plan.num_wgs), dim3(256), 0, stream, a); break;
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_merge_kernel, dim3(num_kv_heads * kGqa * (kHeadDim / kMergeDims), num_seqs),

@@ -40,6 +40,17 @@ __global__ void __launch_bounds__(256) kv_write_kernel(
     const int32_t* __restrict__ token_seq, const int32_t* __restrict__ block_table,
     int32_t bt_stride, int64_t* __restrict__ slot_out) {
   const int32_t i = blockIdx.x;
+  const int64_t src = (int64_t)i * row_elems;
+  const int32_t row_vecs = row_elems / 8;
+  // The new rows do not depend on the slot: load them first so their latency
+  // overlaps the positions -> block table -> slot chain.
+  u32x4 vec[4];
+  int nvec = 0;
+  for (int32_t v = threadIdx.x; v < 2 * row_vecs && nvec < 4; v += 256, ++nvec) {
+    const bool is_v = v >= row_vecs;
+    const int32_t e = (is_v ? v - row_vecs : v) * 8;
+    vec[nvec] = *reinterpret_cast<const u32x4*>((is_v ? v_new : k_new) + src + e);
+  }
   int64_t slot;
   if (slot_mapping) {
     slot = slot_mapping[i];
@@ -52,14 +63,17 @@ __global__ void __launch_bounds__(256) kv_write_kernel(
   const int64_t page = slot / block_size;
   const int64_t row = slot - page * block_size;
   const int64_t dst = page * page_stride + row * row_elems;
-  const int64_t src = (int64_t)i * row_elems;
-  const int32_t row_vecs = row_elems / 8;
-  for (int32_t v = threadIdx.x; v < 2 * row_vecs; v += 256) {
+  int k = 0;
+  for (int32_t v = threadIdx.x; v < 2 * row_vecs; v += 256, ++k) {
     const bool is_v = v >= row_vecs;
     const int32_t e = (is_v ? v - row_vecs : v) * 8;
-    const uint16_t* s = (is_v ? v_new : k_new) + src + e;
-    uint16_t* d = (is_v ? v_cache : k_cache) + dst + e;
-    *reinterpret_cast<u32x4*>(d) = *reinterpret_cast<const u32x4*>(s);
+    u32x4 x;
+    if (k < 4) {
+      x = vec[k];
+    } else {   // rows longer than 4 x 256 vectors (more than 32 KV heads)
+      x = *reinterpret_cast<const u32x4*>((is_v ? v_new : k_new) + src + e);
+    }
+    *reinterpret_cast<u32x4*>((is_v ? v_cache : k_cache) + dst + e) = x;
   }
 }
 

@@ -108,16 +108,19 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t bloc
   if (num_seqs < 1 || num_seqs > 65535 || max_seq_len < 1 ||
       (int64_t)max_seq_len + block_size > INT32_MAX)
     return PA_ERR_SIZE;
-  *bytes_out = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads).bytes;
+  const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads);
+  if (plan.steps_ub >= pa::kMaxDecodeSteps) return PA_ERR_SIZE;
+  *bytes_out = plan.bytes;
   return PA_OK;
 }
 
-int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
-              const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
-              int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
-              int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
-              int32_t num_kv_heads, int32_t head_dim, void* workspace,
-              size_t workspace_bytes, void* stream) {
+static int decode_common(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                         const uint16_t* v_cache, int64_t page_stride,
+                         const int32_t* block_table, int32_t bt_stride,
+                         const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                         int32_t block_size, float scale, int32_t num_q_heads,
+                         int32_t num_kv_heads, int32_t head_dim, void* workspace,
+                         size_t workspace_bytes, const pa::DecodeAppend* append, void* stream) {
   if (!out || !q || !block_table || !seq_lens) return PA_ERR_NULL;
   int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
   if (rc) return rc;
@@ -129,12 +132,39 @@ int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
   if (bt_stride < 1 || (int64_t)bt_stride * block_size < max_seq_len) return PA_ERR_TABLE;
   if (!aligned16(out) || !aligned16(q)) return PA_ERR_ALIGN;
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads);
+  if (plan.steps_ub >= pa::kMaxDecodeSteps) return PA_ERR_SIZE;
   if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
   return launch_status(pa::launch_decode(out, q, k_cache, v_cache, page_stride, block_table,
                                          bt_stride, seq_lens, num_seqs, max_seq_len, block_size,
-                                         scale, num_kv_heads, plan, workspace,
+                                         scale, num_kv_heads, plan, workspace, append,
                                          static_cast<hipStream_t>(stream)));
+}
+
+int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+              const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
+              int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+              int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
+              int32_t num_kv_heads, int32_t head_dim, void* workspace,
+              size_t workspace_bytes, void* stream) {
+  return decode_common(out, q, k_cache, v_cache, page_stride, block_table, bt_stride, seq_lens,
+                       num_seqs, max_seq_len, block_size, scale, num_q_heads, num_kv_heads,
+                       head_dim, workspace, workspace_bytes, nullptr, stream);
+}
+
+int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16_t* v_cache,
+                     int64_t page_stride, const int32_t* block_table, int32_t bt_stride,
+                     const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
+                     int32_t block_size, float scale, int32_t num_q_heads,
+                     int32_t num_kv_heads, int32_t head_dim, const uint16_t* k_new,
+                     const uint16_t* v_new, int64_t* slot_out, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!k_new || !v_new) return PA_ERR_NULL;
+  if (!aligned16(k_new) || !aligned16(v_new)) return PA_ERR_ALIGN;
+  const pa::DecodeAppend append{k_new, v_new, k_cache, v_cache, slot_out};
+  return decode_common(out, q, k_cache, v_cache, page_stride, block_table, bt_stride, seq_lens,
+                       num_seqs, max_seq_len, block_size, scale, num_q_heads, num_kv_heads,
+                       head_dim, workspace, workspace_bytes, &append, stream);
 }
 
 int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int32_t start_pos,

@@ -24,25 +24,42 @@ hipError_t launch_kv_write(uint16_t* k_cache, uint16_t* v_cache, int64_t page_st
 // Decode split plan.  A step is 16 tokens of one page for `heads_per_wg`
 // KV heads (16 * 4 / heads_per_wg tokens when a workgroup's four waves share
 // fewer heads).  The batch's steps are cut into `num_wgs` near-equal ranges.
-constexpr int kDecodeWorkgroups = 256;   // one per MI355X CU
+#ifndef PA_DECODE_WGS
+#define PA_DECODE_WGS 256
+#endif
+constexpr int kDecodeWorkgroups = PA_DECODE_WGS;   // one per MI355X CU
 
 struct DecodePlan {
   int32_t heads_per_wg;
   int32_t step_tokens;
   int32_t steps_per_page;
   int32_t num_wgs;
+  int64_t steps_ub;      // upper bound of the batch's steps (must stay below 2^31)
   size_t meta_off, p_ml_off, p_acc_off, bytes;
 };
+constexpr int64_t kMaxDecodeSteps = (int64_t)1 << 31;
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
                        int32_t num_kv_heads);
+
+// Token appended by the decode launch itself (pa_decode_append): row [s]
+// of k_new / v_new ([num_seqs][num_kv_heads][256]) is the token at position
+// seq_lens[s] - 1; k_cache / v_cache are the same caches the decode reads.
+struct DecodeAppend {
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  uint16_t* k_cache;
+  uint16_t* v_cache;
+  int64_t* slot_out;   // NULL = do not store the slots
+};
 
 hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
                          const uint16_t* v_cache, int64_t page_stride,
                          const int32_t* block_table, int32_t bt_stride,
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                          int32_t block_size, float scale, int32_t num_kv_heads,
-                         const DecodePlan& plan, void* workspace, hipStream_t stream);
+                         const DecodePlan& plan, void* workspace, const DecodeAppend* append,
+                         hipStream_t stream);
 
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32_t start_pos,
                           int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,

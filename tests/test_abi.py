@@ -30,7 +30,8 @@ def _codes():
 def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused",
-                          "pa_decode_workspace_size", "pa_decode", "pa_prefill_chunk",
+                          "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
+                          "pa_prefill_chunk",
                           "pa_strerror", "pa_build_info"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True).stdout
@@ -79,6 +80,31 @@ def test_decode_validation():
     assert _decode(ws=None) == C["PA_ERR_WORKSPACE"]
     need = pa.decode_workspace_size(1, 8193, 832, 4)
     assert _decode(ws_bytes=need - 1) == C["PA_ERR_WORKSPACE"]
+
+
+def _append(**kw):
+    args = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, page_stride=832 * 1024, bt=FAKE, bt_stride=10,
+                seq_lens=FAKE, num_seqs=1, max_seq_len=8193, B=832, scale=0.0625, hq=24, hkv=4,
+                d=256, k_new=FAKE, v_new=FAKE, slot_out=None, ws=FAKE, ws_bytes=1 << 30)
+    args.update(kw)
+    return pa.lib.pa_decode_append(args["out"], args["q"], args["k"], args["v"],
+                                   args["page_stride"], args["bt"], args["bt_stride"],
+                                   args["seq_lens"], args["num_seqs"], args["max_seq_len"],
+                                   args["B"], args["scale"], args["hq"], args["hkv"], args["d"],
+                                   args["k_new"], args["v_new"], args["slot_out"], args["ws"],
+                                   args["ws_bytes"], None)
+
+
+def test_decode_append_validation():
+    assert _append(k_new=None) == C["PA_ERR_NULL"]
+    assert _append(v_new=None) == C["PA_ERR_NULL"]
+    assert _append(v_new=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    assert _append(out=None) == C["PA_ERR_NULL"]
+    assert _append(d=128) == C["PA_ERR_UNSUPPORTED"]
+    assert _append(bt_stride=9) == C["PA_ERR_TABLE"]
+    assert _append(ws=None) == C["PA_ERR_WORKSPACE"]
+    need = pa.decode_workspace_size(1, 8193, 832, 4)
+    assert _append(ws_bytes=need - 1) == C["PA_ERR_WORKSPACE"]
 
 
 def test_workspace_size_monotone():

@@ -148,3 +148,75 @@ def test_workspace_reuse_across_shapes():
     compare(run_gpu(big, ws=ws), run_oracle(big, seqs=range(16)), "reuse-big")
     compare(run_gpu(small, ws=ws), run_oracle(small), "reuse-small")
     compare(run_gpu(small, ws=ws), run_oracle(small), "reuse-small-again")
+
+
+# ---------------------------------------------------------------------------
+# pa_decode_append: the new token's KV write inside the decode launch.
+
+def run_gpu_append(case: W.DecodeCase, ws=None):
+    """Returns (out bits, k cache bits, v cache bits, slots) after one call."""
+    import torch
+    pa = _pa()
+    S = case.q.shape[0]
+    # the appended token of sequence s sits at position seq_lens[s] - 1
+    assert np.array_equal(case.positions, case.seq_lens[case.token_seq].astype(np.int64) - 1)
+    assert np.array_equal(case.token_seq, np.arange(S))
+    k, v = to_dev(case.k_cache), to_dev(case.v_cache)
+    slots = torch.full((S,), -7, dtype=torch.int64, device="cuda")
+    out = pa.decode_append(to_dev(case.q), k, v, to_dev(case.block_tables), to_dev(case.seq_lens),
+                           case.max_seq_len, case.scale, to_dev(case.k_new), to_dev(case.v_new),
+                           workspace=ws, slot_out=slots)
+    _sync()
+    return bits(out), bits(k), bits(v), slots.cpu().numpy()
+
+
+def _check_append(c: W.DecodeCase):
+    got, kc, vc, slots = run_gpu_append(c)
+    ref_slots = oracle.slot_mapping(c.positions, c.token_seq, c.block_tables, c.block_size)
+    assert np.array_equal(slots, ref_slots)
+    k_ref, v_ref = oracle.kv_write(c.k_cache, c.v_cache, c.k_new, c.v_new, ref_slots)
+    assert np.array_equal(kc, k_ref) and np.array_equal(vc, v_ref)     # bit-exact cache
+    compare(got, oracle.decode(c.q, k_ref, v_ref, c.block_tables, c.seq_lens, c.block_size,
+                               c.scale), c.name + " append")
+    # same bits as the two-launch path (kv_write_fused, then decode)
+    assert np.array_equal(got, run_gpu(c))
+
+
+def test_append_8k():
+    c = W.decode_8k()
+    log(c.name + " append")
+    _check_append(c)
+
+
+@pytest.mark.parametrize("B", [784, 1024])
+def test_append_32k(B):
+    """32767 cached tokens + the appended one (seq_len 32768)."""
+    pages = -(-32768 // B)
+    c = W.make_decode_case(f"append_ctx32768_b{B}", 70 + B, [32767], B, pages + 3)
+    log(c.name)
+    _check_append(c)
+
+
+def test_append_batched_16_seqs():
+    c = W.batched_decode()
+    log(c.name + " append")
+    _check_append(c)
+
+
+@pytest.mark.parametrize("B", [832, 64, 16, 1])
+def test_append_ragged_and_page_starts(B):
+    """The appended token as the first row of a fresh page, the last row of a
+    page, and mid-page, with NaN-poisoned unused rows."""
+    lens = sorted({1, 2, 17, 64, 65, B, B + 1, 2 * B, 2 * B + 1, 3 * B - 1} - {0})
+    lens = [n for n in lens if 1 <= n <= 4000]
+    pages = sum(-(-(n + 1) // B) for n in lens)
+    c = W.make_decode_case(f"append_ragged_b{B}", 60 + B, lens, B, pages + 4,
+                           write_new_token=True)
+    log(f"{c.name} lens={lens}")
+    _check_append(c)
+
+
+def test_append_single_kv_head_shard():
+    c = W.make_decode_case("append_hkv1", 11, [4097, 833], 832, 12, hkv=1, hq=6)
+    log(c.name)
+    _check_append(c)
