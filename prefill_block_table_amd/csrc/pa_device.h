@@ -19,16 +19,12 @@ typedef __attribute__((__vector_size__(2 * sizeof(uint32_t)))) uint32_t u32x2;
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
-// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
+// Two fp32 values to packed bf16 (round to nearest even; NaN stays NaN):
+// one gfx950 v_cvt_pk_bf16_f32.
+typedef __bf16 bf16x2_hw __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
-  return f32_to_bf16_rne(lo) | (f32_to_bf16_rne(hi) << 16);
+  const bf16x2_hw v = {(__bf16)lo, (__bf16)hi};
+  return __builtin_bit_cast(uint32_t, v);
 }
 
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }

@@ -30,7 +30,8 @@
 namespace pa {
 
 const char* const kPrefillVariant =
-    "prefill-v2(bm128,bn64,mfma32x32x16,st-orient,lds-dma-kv,2stage,tr16-vt,lazy-rescale,heavy-first)";
+    "prefill-v3(bm128,bn64,mfma32x32x16,st-orient,lds-dma-kv,2stage,tr16-vt,lazy-rescale,heavy-first,"
+    "xcd-kvhead-map,hw-bf16-pack)";
 
 namespace {
 
@@ -43,6 +44,12 @@ constexpr float kRescaleSlack = 8.f;
 
 #define PA_LDS __attribute__((address_space(3)))
 #define PA_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+// Workgroup barrier without a memory fence.  Every wave orders its own
+// direct-to-LDS loads (vmcnt) and LDS operand reads (lgkmcnt) with explicit
+// waits before it arrives; a fenced barrier would in addition wait for the
+// next group's loads, which were issued just before, and so serialize the
+// prefetch with the compute it is meant to overlap.
+#define PA_BARRIER() __builtin_amdgcn_s_barrier()
 
 struct PrefillArgs {
   uint16_t* out;
@@ -93,12 +100,32 @@ __device__ __forceinline__ int vswz(int r) { return (r & 7) << 2; }
 __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
 
-  const int head = blockIdx.x;
-  const int tile = a.num_q_tiles - 1 - (int)blockIdx.y;   // heaviest (latest) rows first
-  const int g = head / kGqa;
+  // Workgroup -> (query head, query tile).  Tiles run heaviest (latest
+  // rows) first.  Consecutive workgroup ids go to the 8 XCDs in turn; when
+  // the KV heads divide the XCDs evenly, every XCD serves one KV head (8 / G
+  // XCDs per head, taking alternate entries of that head's heavy-first
+  // list), so the K/V a workgroup streams are the ones its XCD's L2 already
+  // holds for its neighbours.
+  const int G = a.num_kv_heads;
+  const int T = a.num_q_tiles;
+  const int L = blockIdx.x;
+  int g, head, tile;
+  if (8 % G == 0 && (kGqa * G * T) % 8 == 0) {
+    const int x = L & 7, slot = L >> 3;
+    g = x % G;
+    const int k = slot * (8 / G) + x / G;        // 0 .. 6T-1 within KV head g
+    tile = T - 1 - k / kGqa;
+    head = g * kGqa + k % kGqa;
+  } else {
+    const int Hq_ = G * kGqa;
+    tile = T - 1 - L / Hq_;
+    head = L % Hq_;
+    g = head / kGqa;
+  }
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  // wave index, uniform per wave: LDS destinations and row bases stay scalar
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hh = lane >> 5;
   const int col = lane & 31;
   const int Hq = a.num_kv_heads * kGqa;
@@ -143,52 +170,88 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
   const char* kbase_g = reinterpret_cast<const char*>(a.k_cache + (int64_t)g * kHeadDim);
   const char* vbase_g = reinterpret_cast<const char*>(a.v_cache + (int64_t)g * kHeadDim);
   const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
+  const int64_t page_bytes = a.page_stride * 2;
 
-  // Issue group u into a stage: this wave loads rows 16w .. 16w+15 of K and V
-  // (8 + 8 direct-to-LDS loads of two rows each).  Rows past the group's live
-  // end reload the page's first row (finite; masked out).
-  auto issue = [&](int u, char* st) {
-    const int page = u / upp;
-    const int grp = u - page * upp;
-    const int key0 = page * B + grp * kGroup;
-    const int n = min(kGroup, min(B - grp * kGroup, kv_end - key0));
-    const int64_t poff = (int64_t)load_const_i32(a.block_table + page) * a.page_stride * 2 +
-                         (int64_t)grp * kGroup * rs_bytes;
-    const char* kp = kbase_g + poff;
-    const char* vp = vbase_g + poff;
-    const int pos = lane & 31;
+  // Wave w loads rows 16w .. 16w+15 of each group's K and V tiles: direct-to-
+  // LDS load j moves rows 16w + 2j (lanes 0..31) and 16w + 2j + 1 (lanes
+  // 32..63).  Per-lane byte offsets from the group's first row, with the
+  // chunk swizzle of the destination row, are computed once.
+  const int pos = lane & 31;
+  const int half = lane >> 5;
+  uint32_t koff[8], voff[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int row = 16 * w + 2 * j + (lane >> 5);
-      // signed: a masked row points back at the page's first row
-      const int32_t roff = (row < n ? row : -grp * kGroup) * (int32_t)rs_bytes;
-      __builtin_amdgcn_global_load_lds(kp + roff + ((pos ^ kswz(row)) << 4),
-                                       (PA_LDS void*)(st + row * kRowBytes - (lane >> 5) * kRowBytes),
-                                       16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + roff + ((pos ^ vswz(row)) << 4),
-                                       (PA_LDS void*)(st + kTileBytes + row * kRowBytes - (lane >> 5) * kRowBytes),
-                                       16, 0, 0);
+  for (int j = 0; j < 8; ++j) {
+    const int row = 16 * w + 2 * j + half;
+    koff[j] = (uint32_t)row * rs_bytes + ((uint32_t)(pos ^ kswz(row)) << 4);
+    voff[j] = (uint32_t)row * rs_bytes + ((uint32_t)(pos ^ vswz(row)) << 4);
+  }
+  // Issue cursor: logical page ip, group ig inside it; the block-table entry
+  // is read (a scalar load) when the first group of a new page is prepared.
+  int ip = 0, ig = 0, ip_loaded = -1;
+  int64_t ip_base = 0;
+  // Loads of the group being issued: uniform page bases and row offset, and
+  // whether every row is live.
+  const char* ikp = nullptr;
+  const char* ivp = nullptr;
+  uint32_t igofs = 0;
+  int in_live = kGroup;
+  auto prepare = [&]() {
+    if (ip != ip_loaded) {
+      ip_loaded = ip;
+      ip_base = (int64_t)load_const_i32(a.block_table + ip) * page_bytes;
     }
+    const int key0 = ip * B + ig * kGroup;
+    in_live = min(kGroup, min(B - ig * kGroup, kv_end - key0));
+    ikp = kbase_g + ip_base;
+    ivp = vbase_g + ip_base;
+    igofs = (uint32_t)(ig * kGroup) * rs_bytes;
+    if (++ig == upp) { ig = 0; ++ip; }
+  };
+  // Direct-to-LDS loads j (rows 16w + 2j and 16w + 2j + 1 of K and of V) of
+  // the prepared group into stage st.  Rows past the group's live end reload
+  // the page's first row (finite; masked out).
+  auto row_base = [&](int j) {
+    uint32_t rb = igofs;
+    if (in_live < kGroup) {
+      const int row = 16 * w + 2 * j + half;
+      if (row >= in_live) rb = (uint32_t)(-row) * rs_bytes;      // -> page row 0
+    }
+    return rb;
+  };
+  auto issue_k = [&](int j, char* st) {
+    __builtin_amdgcn_global_load_lds(ikp + (row_base(j) + koff[j]),
+                                     (PA_LDS void*)(st + (16 * w + 2 * j) * kRowBytes), 16, 0, 0);
+  };
+  auto issue_v = [&](int j, char* st) {
+    __builtin_amdgcn_global_load_lds(ivp + (row_base(j) + voff[j]),
+                                     (PA_LDS void*)(st + kTileBytes + (16 * w + 2 * j) * kRowBytes), 16, 0, 0);
+  };
+  auto issue_all = [&](char* st) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) { issue_k(j, st); issue_v(j, st); }
   };
 
   char* st0 = smem;
   char* st1 = smem + kStageBytes;
-  issue(0, st0);
+  prepare();
+  issue_all(st0);
+  int cp = 0, cg = 0;      // compute cursor (page, group)
 
+  // One barrier per group: entering iteration u every wave waits for its own
+  // loads of group u, then the barrier makes all of group u visible and
+  // guarantees every wave has finished group u - 1, whose stage the loads of
+  // group u + 1 then overwrite.
   for (int u = 0; u < units; ++u) {
     char* st = (u & 1) ? st1 : st0;
-    if (u + 1 < units) {
-      issue(u + 1, (u & 1) ? st0 : st1);
-      PA_WAIT_VMCNT(16);      // this wave's part of group u has landed
-    } else {
-      PA_WAIT_VMCNT(0);
-    }
-    __syncthreads();          // every wave's part of group u has landed
+    char* nst = (u & 1) ? st0 : st1;
+    PA_WAIT_VMCNT(0);         // this wave's part of group u has landed
+    PA_BARRIER();             // every wave's part of group u has landed
+    const bool more = u + 1 < units;
+    if (more) prepare();
 
-    const int page = u / upp;
-    const int grp = u - page * upp;
-    const int key0 = page * B + grp * kGroup;
-    const int n = min(kGroup, min(B - grp * kGroup, kv_end - key0));
+    const int key0 = cp * B + cg * kGroup;
+    const int n = min(kGroup, min(B - cg * kGroup, kv_end - key0));
+    if (++cg == upp) { cg = 0; ++cp; }
     const uint32_t kt = lds_addr(st);
     const uint32_t vt = kt + kTileBytes;
 
@@ -212,6 +275,11 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int bt = 0; bt < 8; ++bt) {
         const int cur = bt & 1;
+        // wave w's loads of the next group go out at its own point of the
+        // group's work (waves 0 and 1 during S^T, 2 and 3 during PV): the
+        // CU's load path then serves one wave at a time, and a wave waiting
+        // for it leaves the other three computing
+        if (more && bt == 4 * w) issue_all(nst);
         if (bt < 7) {
           kread(2 * bt + 2, kb[cur ^ 1][0], kb[cur ^ 1][1]);
           kread(2 * bt + 3, kb[cur ^ 1][2], kb[cur ^ 1][3]);
@@ -303,6 +371,7 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
         for (int i = 0; i < 4; ++i) vread(i, va[0][i]);
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
+          if (more && half == 0 && 2 * ks == 4 * (w - 2)) issue_all(nst);
           if (half == 0) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) vread(4 + i, va[1][i]);
@@ -323,7 +392,6 @@ __global__ void __launch_bounds__(256, 1) prefill_kernel(PrefillArgs a) {
         }
       }
     }
-    __syncthreads();          // all waves are done with this stage before it is refilled
   }
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
@@ -362,7 +430,7 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   a.scale_log2 = scale * 1.4426950408889634f;
   a.num_kv_heads = num_kv_heads;
   a.num_q_tiles = (q_len + kBM - 1) / kBM;
-  hipLaunchKernelGGL(prefill_kernel, dim3(num_kv_heads * kGqa, a.num_q_tiles), dim3(256), 0,
+  hipLaunchKernelGGL(prefill_kernel, dim3(num_kv_heads * kGqa * a.num_q_tiles), dim3(256), 0,
                      stream, a);
   return hipGetLastError();
 }
