@@ -103,12 +103,14 @@ __device__ __forceinline__ float pair32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// 16-byte chunk c of K row r sits at position c ^ (r & 7): the 8 rows an
-// operand read touches at a time hit 8 different bank groups.  V row r: chunk
-// c at c ^ ((r & 3) << 1): the 4 rows of a transposing read hit 4 different
-// 32-byte bank groups.
-__device__ __forceinline__ int kswz(int r) { return r & 7; }
-__device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
+// LDS rows are 512 bytes, so every row starts at the same bank.  16-byte
+// chunk c of K row r sits at position c ^ (r & 15): the 16 rows one pass of
+// an operand read touches (16 lanes x 16 B) land on 16 different 16-byte
+// bank groups.  V row r: chunk c at c ^ ((r & 7) << 1): the 8 rows one pass
+// of a transposing read touches (32 lanes, 8 rows x 32 B) land on 8
+// different 32-byte bank groups.
+__device__ __forceinline__ int kswz(int r) { return r & 15; }
+__device__ __forceinline__ int vswz(int r) { return (r & 7) << 1; }
 
 // LDS operand reads the compiler does not track (it cannot tell which
 // direct-to-LDS load wrote which bytes and would drain the prefetched group
@@ -227,22 +229,25 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
 
   // Per-lane operand read offsets within a stage.
   // K A-operand (16x16x32) of key block kb and d-step ds: row 16*kb + c16,
-  // 16-byte chunk 4*ds + kq, stored at (4*ds + kq) ^ (c16 & 7)
-  // = 8*(ds >> 1) + 4*((ds & 1) ^ ((c16 >> 2) & 1)) + (kq ^ (c16 & 3)).
-  const uint32_t k_even = c16 * kRowBytes + ((((c16 >> 2) & 1) * 4 + (kq ^ (c16 & 3))) << 4);
-  const uint32_t k_odd = c16 * kRowBytes + (((((c16 >> 2) & 1) ^ 1) * 4 + (kq ^ (c16 & 3))) << 4);
+  // 16-byte chunk 4*ds + kq, stored at (4*ds + kq) ^ c16
+  // = 16*(ds >> 2) + 4*((ds & 3) ^ (c16 >> 2)) + (kq ^ (c16 & 3)):
+  // base k_t[ds & 3], immediate 8192*kb + 256*(ds >> 2).
+  uint32_t k_t[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    k_t[t] = c16 * kRowBytes + ((4 * (t ^ (c16 >> 2)) + (kq ^ (c16 & 3))) << 4);
   // V^T A-operand of d-block db and key step ks (keys 32*ks ..): transposing
   // reads, lane (kq, j = c16) pointing at V[k0 + (j >> 2)][16*db + 4*(j & 3)]
   // with k0 = 32*ks + 4*kq (first read, k = 0..3 of the operand) and
-  // k0 + 16 (second read, k = 4..7).  Row r = k0 + (j >> 2) has r & 3 =
-  // (j >> 2) & 3 =: m, so chunk 2*db + ((j & 3) >> 1) sits at
-  // 2*((db & ~3) + ((db & 3) ^ m)) + ((j & 3) >> 1).
-  const int vm = (c16 >> 2) & 3;
+  // k0 + 16 (second read, k = 4..7).  Row r = k0 + (j >> 2) has r & 7 =
+  // 4*(kq & 1) + (j >> 2) =: m, so chunk 2*db + ((j & 3) >> 1) sits at
+  // 2*(8*(db >> 3) + ((db & 7) ^ m)) + ((j & 3) >> 1): base v_t[db & 7],
+  // immediate 256*(db >> 3) + 512*k0's multiple of 16.
+  const int vm = 4 * (kq & 1) + (c16 >> 2);
   const uint32_t vrow = (uint32_t)(4 * kq + (c16 >> 2)) * kRowBytes + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
-  const uint32_t v_t0 = kTileBytes + vrow + ((0 ^ vm) << 5);
-  const uint32_t v_t1 = kTileBytes + vrow + ((1 ^ vm) << 5);
-  const uint32_t v_t2 = kTileBytes + vrow + ((2 ^ vm) << 5);
-  const uint32_t v_t3 = kTileBytes + vrow + ((3 ^ vm) << 5);
+  uint32_t v_t[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) v_t[t] = kTileBytes + vrow + ((t ^ vm) << 5);
 
   char* st0 = smem;
   char* st1 = smem + kStageBytes;
@@ -274,20 +279,22 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
     {
-      const uint32_t ke = sbase + k_even, ko = sbase + k_odd;
+      const uint32_t k0a = sbase + k_t[0], k1a = sbase + k_t[1], k2a = sbase + k_t[2], k3a = sbase + k_t[3];
       u32x4 kv[2][4];
-      // d-step ds: base by ds & 1, immediate kb * 8192 + (ds >> 1) * 128
+      // d-step ds: base k_t[ds & 3], immediate kb * 8192 + (ds >> 2) * 256
       auto kread = [&](int ds, u32x4 (&d)[4]) {
         switch (ds) {
+#define PA_KB(DS) (((DS) & 3) == 0 ? k0a : ((DS) & 3) == 1 ? k1a : ((DS) & 3) == 2 ? k2a : k3a)
 #define PA_KR(DS)                                                                  \
   case DS:                                                                         \
-    PA_DS_READ_B128(d[0], ((DS) & 1) ? ko : ke, 0 * 8192 + ((DS) >> 1) * 128);     \
-    PA_DS_READ_B128(d[1], ((DS) & 1) ? ko : ke, 1 * 8192 + ((DS) >> 1) * 128);     \
-    PA_DS_READ_B128(d[2], ((DS) & 1) ? ko : ke, 2 * 8192 + ((DS) >> 1) * 128);     \
-    PA_DS_READ_B128(d[3], ((DS) & 1) ? ko : ke, 3 * 8192 + ((DS) >> 1) * 128);     \
+    PA_DS_READ_B128(d[0], PA_KB(DS), 0 * 8192 + ((DS) >> 2) * 256);                \
+    PA_DS_READ_B128(d[1], PA_KB(DS), 1 * 8192 + ((DS) >> 2) * 256);                \
+    PA_DS_READ_B128(d[2], PA_KB(DS), 2 * 8192 + ((DS) >> 2) * 256);                \
+    PA_DS_READ_B128(d[3], PA_KB(DS), 3 * 8192 + ((DS) >> 2) * 256);                \
     break;
           PA_KR(0) PA_KR(1) PA_KR(2) PA_KR(3) PA_KR(4) PA_KR(5) PA_KR(6) PA_KR(7)
 #undef PA_KR
+#undef PA_KB
         }
       };
       kread(0, kv[0]);
@@ -362,20 +369,25 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     // O^T += V^T P^T: d-block db, key step ks.  The reads of a batch (four
     // d-blocks, one key step) run one batch ahead of its MFMAs.
     {
-      const uint32_t w0 = sbase + v_t0, w1 = sbase + v_t1, w2 = sbase + v_t2, w3 = sbase + v_t3;
+      uint32_t wv[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) wv[t] = sbase + v_t[t];
       u32x2 va[2][4][2];
-      // batch b = 2*dg + ks: d-blocks 4*dg .. 4*dg+3 (immediate 128*dg), keys
-      // 32*ks + 4*kq (immediate 32*ks*512) and + 16 (another 16*512)
+      // batch b = 2*dg + ks: d-blocks 4*dg .. 4*dg+3 (bases v_t[4*(dg & 1) + t],
+      // immediate 256*(dg >> 1)), keys 32*ks + 4*kq (immediate 32*ks*512) and
+      // + 16 (another 16*512)
       auto vread = [&](int b, u32x2 (&d)[4][2]) {
         switch (b) {
 #define PA_VR(BB)                                                                        \
   case BB: {                                                                             \
-    constexpr int off0 = 128 * ((BB) >> 1) + 32 * ((BB) & 1) * kRowBytes;               \
+    constexpr int dg = (BB) >> 1;                                                        \
+    constexpr int off0 = 256 * (dg >> 1) + 32 * ((BB) & 1) * kRowBytes;                  \
     constexpr int off1 = off0 + 16 * kRowBytes;                                          \
-    PA_DS_READ_TR16(d[0][0], w0, off0); PA_DS_READ_TR16(d[0][1], w0, off1);              \
-    PA_DS_READ_TR16(d[1][0], w1, off0); PA_DS_READ_TR16(d[1][1], w1, off1);              \
-    PA_DS_READ_TR16(d[2][0], w2, off0); PA_DS_READ_TR16(d[2][1], w2, off1);              \
-    PA_DS_READ_TR16(d[3][0], w3, off0); PA_DS_READ_TR16(d[3][1], w3, off1);              \
+    constexpr int tb = 4 * (dg & 1);                                                     \
+    PA_DS_READ_TR16(d[0][0], wv[tb + 0], off0); PA_DS_READ_TR16(d[0][1], wv[tb + 0], off1); \
+    PA_DS_READ_TR16(d[1][0], wv[tb + 1], off0); PA_DS_READ_TR16(d[1][1], wv[tb + 1], off1); \
+    PA_DS_READ_TR16(d[2][0], wv[tb + 2], off0); PA_DS_READ_TR16(d[2][1], wv[tb + 2], off1); \
+    PA_DS_READ_TR16(d[3][0], wv[tb + 3], off0); PA_DS_READ_TR16(d[3][1], wv[tb + 3], off1); \
   } break;
           PA_VR(0) PA_VR(1) PA_VR(2) PA_VR(3) PA_VR(4) PA_VR(5) PA_VR(6) PA_VR(7)
 #undef PA_VR
@@ -398,7 +410,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         const int dg = b >> 1, ks = b & 1;
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          // d-block 4*dg + t (t = db & 3 picks the read base)
+          // d-block 4*dg + t
           const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
           o[4 * dg + t] = mfma16(av, pb[ks], o[4 * dg + t]);
         }
