@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-extra", action="store_true", help="headline workload only")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--prefill-pass", action="store_true",
+                    help="for rocprofv3 --pmc runs: 5 launches of each prefill chunk")
     ap.add_argument("--counter-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a few headline decode steps, then a "
                          "256 MiB device-to-device copy that calibrates FETCH_SIZE/WRITE_SIZE")
@@ -217,16 +219,22 @@ def bench_prefill(D, pa, case, steps, warmup):
             pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
 
         def step(i, ev):
-            ev[0].record()
+            if ev is not None:
+                ev[0].record()
             pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
-            ev[1].record()
+            if ev is not None:
+                ev[1].record()
 
-        total_ms, kern, host_s = timed_loop(torch, steps, step, 5.0)
+        # device time per launch of back-to-back launches (the figure), then
+        # per-launch event brackets for the spread
+        hold = 2.0 * steps + 5.0
+        total_ms, _, _ = timed_loop(torch, steps, step, hold, events=False)
+        _, kern, _ = timed_loop(torch, steps, step, hold)
         st = _stats(kern)
-        avg = st["kernel_ms_avg"]
+        avg = total_ms / steps
         fl = causal_flops(ch.start_pos, ch.q_len)
         out[f"q{ch.q_len}_start{ch.start_pos}"] = dict(
-            st, causal_flops=fl, tflops=fl / (avg * 1e-3) / 1e12,
+            st, ms_per_launch=avg, causal_flops=fl, tflops=fl / (avg * 1e-3) / 1e12,
             frac_bf16_peak=fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             kv_write_ms=w0.elapsed_time(w1), kv_write_bytes=ch.q_len * 4 * 256 * 2 * 2)
     return out
@@ -274,6 +282,20 @@ def counter_pass(D, pa, W):
     torch.cuda.synchronize()
 
 
+def prefill_pass(D, pa, W):
+    """Launch sequence profiled by the prefill --pmc runs: each chunk of the
+    8K prefill workload 5 times (K/V already in the cache)."""
+    torch = D.torch
+    case = W.prefill_8k()
+    k, v, bt = D.t(case.k_cache), D.t(case.v_cache), D.t(case.block_table)
+    for ch in case.chunks:
+        q = D.t(ch.q)
+        o = torch.empty_like(q)
+        for _ in range(5):
+            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
+        torch.cuda.synchronize()
+
+
 def cpu_baseline(case, seconds):
     """The fp64 oracle on the headline workload, repeated for ~`seconds`."""
     import oracle
@@ -313,6 +335,9 @@ def main():
     print(f"[bench] {pa.build_info()}", file=sys.stderr, flush=True)
     if args.counter_pass:
         counter_pass(D, pa, W)
+        return
+    if args.prefill_pass:
+        prefill_pass(D, pa, W)
         return
 
     head_case = W.decode_8k()
