@@ -283,12 +283,15 @@ def counter_pass(D, pa, W):
 
 
 def prefill_pass(D, pa, W):
-    """Launch sequence profiled by the prefill --pmc runs: each chunk of the
-    8K prefill workload 5 times (K/V already in the cache)."""
+    """Launch sequence profiled by the prefill --pmc runs: per chunk of the
+    8K prefill workload, the chunk's KV write, then 5 attention launches."""
     torch = D.torch
+    np = D.np
     case = W.prefill_8k()
     k, v, bt = D.t(case.k_cache), D.t(case.v_cache), D.t(case.block_table)
     for ch in case.chunks:
+        pos = D.t(np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64))
+        pa.kv_write_fused(k, v, D.t(ch.k_new), D.t(ch.v_new), pos, bt)
         q = D.t(ch.q)
         o = torch.empty_like(q)
         for _ in range(5):

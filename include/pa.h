@@ -64,6 +64,7 @@ extern "C" {
 #define PA_ERR_STRIDE -7        /* page_stride smaller than one page */
 #define PA_ERR_ALIGN -8         /* a bf16 tensor is not 16-byte aligned */
 #define PA_ERR_LAUNCH -9        /* the HIP runtime rejected a kernel launch */
+#define PA_ERR_SCALE -10        /* scale is not a positive finite number */
 
 /*
  * Slot mapping ([PREP] §3.2 and §5): for each token i,
@@ -145,9 +146,10 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t bloc
  *               <= bt_stride * block_size.
  * workspace     device buffer of >= pa_decode_workspace_size(...) bytes,
  *               256-byte aligned, contents arbitrary (see above).
+ * scale         positive and finite (1/sqrt(256) for the usual softmax).
  * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE
  * (num_seqs < 1, max_seq_len < 1), PA_ERR_TABLE, PA_ERR_STRIDE,
- * PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_LAUNCH.
+ * PA_ERR_WORKSPACE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
  */
 int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
               const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
@@ -198,8 +200,9 @@ int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16
  * block_table    int32 [num_table_entries] (one sequence's row);
  *                ceil((start_pos + q_len) / block_size) <= num_table_entries.
  * q_len >= 1, start_pos >= 0, start_pos + q_len < 2^31.
+ * scale          positive and finite.
  * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE,
- * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_LAUNCH.
+ * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
  */
 int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int32_t start_pos,
                      int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,

@@ -4,6 +4,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdint>
 #include <cstdio>
 #include <string>
@@ -17,6 +18,10 @@
 namespace {
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// The kernels take each row's maximum of the unscaled scores, which is the
+// maximum of the scaled ones only for a positive scale.
+bool scale_ok(float scale) { return scale > 0.f && scale <= 3.4e38f; }
 
 int check_heads(int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
   if (head_dim != pa::kHeadDimAbi) return PA_ERR_UNSUPPORTED;
@@ -122,6 +127,7 @@ static int decode_common(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          int32_t num_kv_heads, int32_t head_dim, void* workspace,
                          size_t workspace_bytes, const pa::DecodeAppend* append, void* stream) {
   if (!out || !q || !block_table || !seq_lens) return PA_ERR_NULL;
+  if (!scale_ok(scale)) return PA_ERR_SCALE;
   int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
   if (rc) return rc;
   rc = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -173,6 +179,7 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                      int32_t block_size, float scale, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, void* stream) {
   if (!out || !q_chunk || !block_table) return PA_ERR_NULL;
+  if (!scale_ok(scale)) return PA_ERR_SCALE;
   int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
   if (rc) return rc;
   rc = check_heads(num_q_heads, num_kv_heads, head_dim);
@@ -199,6 +206,7 @@ const char* pa_strerror(int code) {
     case PA_ERR_TABLE: return "the block table has fewer entries than the lengths need";
     case PA_ERR_STRIDE: return "page_stride is smaller than one page";
     case PA_ERR_ALIGN: return "a tensor is not aligned (bf16 tensors: 16 bytes, workspace: 256 bytes)";
+    case PA_ERR_SCALE: return "scale must be a positive finite number";
     case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
     default: return "unknown error code";
   }

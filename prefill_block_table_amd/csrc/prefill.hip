@@ -6,16 +6,20 @@
 // allows, none added that it forbids ([ALIGN] §5, §9).
 //
 // Work decomposition (ours): a workgroup of 8 wave64s owns a 128-row query
-// tile of one query head; wave w owns 16 rows, and two waves share each SIMD
-// so that one wave's LDS reads, soft-max and barrier waits overlap the other
-// wave's MFMAs.  Keys stream through LDS one 64-token group of one page at a
-// time (the page's tail group is masked when the page size is not a multiple
-// of 64).  Per group and wave:
-//   S^T[64 keys x 16 rows] = K[64 x 256] Q^T     (32 MFMA 16x16x32)
-//   online softmax on S^T: each lane holds 16 scores of one query row, so
+// tile of one query head.  Waves w and w + 4 (which share a SIMD) own the
+// same 32 query rows; in every 64-token key group wave w takes keys 0..31
+// and wave w + 4 keys 32..63, each with its own online soft-max, and the two
+// halves are merged once at the end.  Each K or V operand read from LDS so
+// feeds two MFMAs (two 16-row blocks), half the LDS traffic per flop of a
+// 16-row wave, and the two waves of a SIMD overlap each other's LDS reads,
+// soft-max and waits with MFMAs.  Keys stream through LDS one 64-token group
+// of one page at a time (the page's tail group is masked when the page size
+// is not a multiple of 64).  Per group and wave, for row blocks rb = 0, 1:
+//   S^T[32 keys x 16 rows] = K[32 x 256] Q_rb^T    (16 MFMA 16x16x32)
+//   online softmax on S^T: each lane holds 8 scores of one query row, so
 //   the row max and sum take two cross-lane swaps; the accumulator is
 //   re-based only when the max grows by more than 2^8
-//   O^T[256 x 16 rows] += V^T[256 x 64] P^T      (32 MFMA 16x16x32)
+//   O_rb^T[256 x 16 rows] += V^T[256 x 32] P_rb^T  (16 MFMA 16x16x32)
 // The transposed orientation makes P^T's MFMA operand a register-local
 // reinterpretation of S^T's accumulator (keys in the order the accumulator
 // holds them; V^T's operand reads use the same order).  K and V rows go from
@@ -23,9 +27,12 @@
 // next group is in flight while this one is computed), 16-byte chunks
 // XOR-swizzled by row so operand reads are bank-conflict free; V^T operands
 // come out of LDS with the gfx950 transposing read.  Groups entirely above
-// the causal diagonal of the tile are never visited; the mask is evaluated
-// only on groups that cross the diagonal or end a page early.
+// the causal diagonal of the tile are never visited, a wave skips a key half
+// that lies wholly above its rows, and the mask is evaluated only on groups
+// that cross the diagonal or end a page early.
 #include <math.h>
+
+#include <type_traits>
 
 #include "pa_device.h"
 #include "pa_internal.h"
@@ -33,19 +40,27 @@
 namespace pa {
 
 const char* const kPrefillVariant =
-    "prefill-v5(bm128,8waves-16rows,2waves-per-simd,bn64,mfma16x16x32,st-orient,lds-dma-kv,2stage,"
+    "prefill-v8(bm128,8waves,pairs-32rows-keyhalves,adjacent-pairs,lean-softmax,bn64,mfma16x16x32,st-orient,lds-dma-kv,2stage,"
     "tr16-vt,lazy-rescale,heavy-first,xcd-kvhead-map,hw-bf16-pack)";
 
 namespace {
 
 constexpr int kWavesPf = 8;
-constexpr int kRowsPerWave = 16;
-constexpr int kBM = kWavesPf * kRowsPerWave;        // 128 query rows per workgroup
+constexpr int kRowsPerWave = 32;                    // two 16-row MFMA blocks
+constexpr int kBM = (kWavesPf / 2) * kRowsPerWave;  // 128 query rows per workgroup
+constexpr int kHalfKeys = kGroup / 2;               // keys per wave per group
 constexpr int kRowBytes = kHeadDim * 2;             // one KV head's row: 512 B
 constexpr int kTileBytes = kGroup * kRowBytes;      // 64 rows: 32 KB
 constexpr int kStageBytes = 2 * kTileBytes;         // K tile then V tile
-constexpr int kSmemBytes = 2 * kStageBytes;         // two stages: 128 KB
+constexpr int kLoopBytes = 2 * kStageBytes;         // two stages: 128 KB
+// End merge: every wave hands its partner the half of O^T the partner
+// finishes (2 row blocks x 8 d-blocks x 64 lanes x 16 B) plus (m, l).
+constexpr int kXoWaveBytes = 2 * 8 * 64 * 16;
+constexpr int kMlOff = kWavesPf * kXoWaveBytes;
+constexpr int kSmemBytes = kMlOff + kWavesPf * 2 * 64 * 8 > kLoopBytes ? kMlOff + kWavesPf * 2 * 64 * 8
+                                                                       : kLoopBytes;
 constexpr float kRescaleSlack = 8.f;
+constexpr float kMinusHuge = -1e30f;
 
 #define PA_LDS __attribute__((address_space(3)))
 #define PA_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
@@ -67,7 +82,8 @@ struct PrefillArgs {
   int32_t start_pos;
   int32_t causal;
   int32_t block_size;
-  float scale_log2;
+  float scale_log2;        // scale * log2(e) (> 0)
+  float inv_scale_log2;    // its reciprocal
   int32_t num_kv_heads;
   int32_t num_q_tiles;
 };
@@ -103,6 +119,26 @@ __device__ __forceinline__ float pair32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Plain v_max_f32 / v_max3_f32.  The scores are never NaN, so the operand
+// quieting that fmaxf adds under IEEE mode (one extra instruction per
+// input) is not needed.
+// x.lo + x.hi (two bf16) + acc in fp32.
+__device__ __forceinline__ float dot2_ones(uint32_t x, float acc) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t one = {(__bf16)1.0f, (__bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x), one, acc, false);
+}
+__device__ __forceinline__ float vmax(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float vmax3(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // LDS rows are 512 bytes, so every row starts at the same bank.  16-byte
 // chunk c of K row r sits at position c ^ (r & 15): the 16 rows one pass of
 // an operand read touches (16 lanes x 16 B) land on 16 different 16-byte
@@ -111,6 +147,14 @@ __device__ __forceinline__ float pair32_sum(float x) {
 // different 32-byte bank groups.
 __device__ __forceinline__ int kswz(int r) { return r & 15; }
 __device__ __forceinline__ int vswz(int r) { return (r & 7) << 1; }
+
+// Lane index read afresh at the point of use: values derived from it are
+// recomputed (a few VALU ops) instead of being held in registers.
+__device__ __forceinline__ int lane_here() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
 
 // LDS operand reads the compiler does not track (it cannot tell which
 // direct-to-LDS load wrote which bytes and would drain the prefetched group
@@ -149,7 +193,8 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int lane = tid & 63;
   // wave index, uniform per wave: LDS destinations and row bases stay scalar
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int c16 = lane & 15;     // this lane's query row within the wave (S^T / O^T column)
+  const int kh = w & 1;         // key half of every group this wave takes
+  const int c16 = lane & 15;     // this lane's query row within a 16-row block
   const int kq = lane >> 4;      // lane group: keys 4*kq .. 4*kq+3 of each 16-key block
   const int Hq = a.num_kv_heads * kGqa;
   const int64_t row_stride = (int64_t)a.num_kv_heads * kHeadDim;
@@ -157,21 +202,29 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int B = a.block_size;
 
   const int q0 = tile * kBM;
-  const int my_row = q0 + kRowsPerWave * w + c16;
-  const bool row_ok = my_row < a.q_len;
-  const int my_pos = a.start_pos + my_row;
-  const int wave_first_pos = a.start_pos + q0 + kRowsPerWave * w;
+  const int wrow0 = q0 + kRowsPerWave * (w >> 1);            // first query row of this wave
+  const int wave_rows = max(0, min(kRowsPerWave, a.q_len - wrow0));
+  const int wave_first_pos = a.start_pos + wrow0;
+  const int wave_last_pos = wave_first_pos + wave_rows - 1;
+  int my_row[2];
+  bool row_ok[2];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    my_row[rb] = wrow0 + 16 * rb + c16;
+    row_ok[rb] = my_row[rb] < a.q_len;
+  }
 
   // Q^T as the B operand of S^T = K Q^T (16x16x32): lane supplies column
   // n = c16 (its query row) and k = 8*kq + i of d-step ds -> d = 32*ds + 8*kq + i.
-  u32x4 qb[8];
-  {
-    const uint16_t* qp = a.q + (int64_t)(row_ok ? my_row : 0) * q_stride + head * kHeadDim + 8 * kq;
+  u32x4 qb[2][8];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const uint16_t* qp = a.q + (int64_t)(row_ok[rb] ? my_row[rb] : 0) * q_stride + head * kHeadDim + 8 * kq;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = load16(qp + 32 * ds);
-      qb[ds] = v;
+      if (row_ok[rb]) v = load16(qp + 32 * ds);
+      qb[rb][ds] = v;
     }
   }
 
@@ -182,20 +235,31 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int last_page = (kv_end - 1) / B;
   const int units = last_page * upp + (kv_end - last_page * B + kGroup - 1) / kGroup;
 
-  // O^T accumulator: d-block db (16 d), register r -> d = 16*db + 4*kq + r of
-  // query row c16.
-  f32x4 o[16];
+  // O^T accumulators: row block rb, d-block db (16 d), register r -> d =
+  // 16*db + 4*kq + r of query row 16*rb + c16.
+  f32x4 o[16][2];
 #pragma unroll
-  for (int db = 0; db < 16; ++db) o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY;    // reference the accumulator is scaled to
-  float l_run = 0.f;          // this lane's partial row sum (its 16 keys per group)
+  for (int db = 0; db < 16; ++db)
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) o[db][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Reference the accumulator is scaled to (log2 units).  It starts at a
+  // finite sentinel far below any score, so -m_run is always a usable
+  // exponent offset: the first live score re-bases it, and masked scores
+  // (-inf) give exp2(-inf) = 0 whatever it is.
+  float m_run[2] = {kMinusHuge, kMinusHuge};
+  float l_run[2] = {0.f, 0.f};               // this lane's partial row sums (8 keys per group)
 
   const char* kbase_g = reinterpret_cast<const char*>(a.k_cache + (int64_t)g * kHeadDim);
   const char* vbase_g = reinterpret_cast<const char*>(a.v_cache + (int64_t)g * kHeadDim);
   const uint32_t rs_bytes = (uint32_t)(row_stride * 2);
   const int64_t page_bytes = a.page_stride * 2;
-  const int pos = lane & 31;
-  const int half = lane >> 5;
+  // Per-lane parts of the load source offsets.  Lane (half, pos) loads
+  // 16-byte chunk pos of row 8w + 2j + half; the K swizzle (row & 15) is
+  // 8*(w & 1) | 2j | half and the V swizzle ((row & 7) << 1) is 4j | 2*half,
+  // so chunk positions are a per-lane base XOR a per-j constant.  Row
+  // strides are multiples of 512 bytes, clear of the chunk bits.
+  // (All per-lane values here are derived from a fresh lane index inside
+  // issue() so that none is held in a register across the loop.)
 
   // Issue cursor: logical page ip, group ig inside it; the block-table entry
   // is read (a scalar load) when the first group of a new page is issued.
@@ -214,40 +278,54 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     const uint32_t gofs = (uint32_t)(ig * kGroup) * rs_bytes;
     const char* kp = kbase_g + ip_base;
     const char* vp = vbase_g + ip_base;
+    const int ln = lane_here(), pos = ln & 31, half = ln >> 5;
+    if (live == kGroup) {
+      const uint32_t k_src = (uint32_t)half * rs_bytes + ((uint32_t)(pos ^ (8 * (w & 1) + half)) << 4);
+      const uint32_t v_src = (uint32_t)half * rs_bytes + ((uint32_t)(pos ^ (2 * half)) << 4);
+      // whole group: every row is live; row offsets are scalar
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int row = 8 * w + 2 * j + half;
-      const uint32_t rb = row < live ? gofs + (uint32_t)row * rs_bytes : 0u;
-      char* dst = st + (8 * w + 2 * j) * kRowBytes;
-      __builtin_amdgcn_global_load_lds(kp + (rb + ((uint32_t)(pos ^ kswz(row)) << 4)),
-                                       (PA_LDS void*)dst, 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vp + (rb + ((uint32_t)(pos ^ vswz(row)) << 4)),
-                                       (PA_LDS void*)(dst + kTileBytes), 16, 0, 0);
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t rowofs = gofs + (uint32_t)(8 * w + 2 * j) * rs_bytes;
+        char* dst = st + (8 * w + 2 * j) * kRowBytes;
+        __builtin_amdgcn_global_load_lds(kp + rowofs + (k_src ^ (32u * j)), (PA_LDS void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + rowofs + (v_src ^ (64u * j)), (PA_LDS void*)(dst + kTileBytes),
+                                         16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int row = 8 * w + 2 * j + half;
+        const uint32_t rb = row < live ? gofs + (uint32_t)row * rs_bytes : 0u;
+        char* dst = st + (8 * w + 2 * j) * kRowBytes;
+        __builtin_amdgcn_global_load_lds(kp + (rb + ((uint32_t)(pos ^ kswz(row)) << 4)),
+                                         (PA_LDS void*)dst, 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + (rb + ((uint32_t)(pos ^ vswz(row)) << 4)),
+                                         (PA_LDS void*)(dst + kTileBytes), 16, 0, 0);
+      }
     }
     if (++ig == upp) { ig = 0; ++ip; }
   };
 
-  // Per-lane operand read offsets within a stage.
-  // K A-operand (16x16x32) of key block kb and d-step ds: row 16*kb + c16,
-  // 16-byte chunk 4*ds + kq, stored at (4*ds + kq) ^ c16
+  // Per-lane operand read offsets within a stage (this wave's key half is
+  // rows 32*kh .. 32*kh+31 of the tile).
+  // Stage bases are multiples of 64 KB, so the swizzled bits of an operand
+  // address are XORed onto one per-lane base.
+  // K A-operand (16x16x32) of key block kb and d-step ds: row 32*kh + 16*kb
+  // + c16, 16-byte chunk 4*ds + kq, stored at (4*ds + kq) ^ c16
   // = 16*(ds >> 2) + 4*((ds & 3) ^ (c16 >> 2)) + (kq ^ (c16 & 3)):
-  // base k_t[ds & 3], immediate 8192*kb + 256*(ds >> 2).
-  uint32_t k_t[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t)
-    k_t[t] = c16 * kRowBytes + ((4 * (t ^ (c16 >> 2)) + (kq ^ (c16 & 3))) << 4);
-  // V^T A-operand of d-block db and key step ks (keys 32*ks ..): transposing
-  // reads, lane (kq, j = c16) pointing at V[k0 + (j >> 2)][16*db + 4*(j & 3)]
-  // with k0 = 32*ks + 4*kq (first read, k = 0..3 of the operand) and
-  // k0 + 16 (second read, k = 4..7).  Row r = k0 + (j >> 2) has r & 7 =
-  // 4*(kq & 1) + (j >> 2) =: m, so chunk 2*db + ((j & 3) >> 1) sits at
-  // 2*(8*(db >> 3) + ((db & 7) ^ m)) + ((j & 3) >> 1): base v_t[db & 7],
-  // immediate 256*(db >> 3) + 512*k0's multiple of 16.
+  // address k_lane ^ ((ds & 3) << 6), immediate 8192*kb + 256*(ds >> 2).
+  const uint32_t k_lane = kh * (kHalfKeys * kRowBytes) + c16 * kRowBytes +
+                          ((4 * (c16 >> 2) + (kq ^ (c16 & 3))) << 4);
+  // V^T A-operand of d-block db: transposing reads, lane (kq, j = c16)
+  // pointing at V[k0 + (j >> 2)][16*db + 4*(j & 3)] with k0 = 32*kh + 4*kq
+  // (first read, k = 0..3 of the operand) and k0 + 16 (second read, k =
+  // 4..7).  Row r = k0 + (j >> 2) has r & 7 = 4*(kq & 1) + (j >> 2) =: m,
+  // so chunk 2*db + ((j & 3) >> 1) sits at 2*(8*(db >> 3) + ((db & 7) ^ m))
+  // + ((j & 3) >> 1): address v_lane ^ ((db & 7) << 5), immediate
+  // 256*(db >> 3) (+ 16 rows).
   const int vm = 4 * (kq & 1) + (c16 >> 2);
-  const uint32_t vrow = (uint32_t)(4 * kq + (c16 >> 2)) * kRowBytes + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
-  uint32_t v_t[8];
-#pragma unroll
-  for (int t = 0; t < 8; ++t) v_t[t] = kTileBytes + vrow + ((t ^ vm) << 5);
+  const uint32_t v_lane = kTileBytes + (uint32_t)(kHalfKeys * kh + 4 * kq + (c16 >> 2)) * kRowBytes +
+                          (vm << 5) + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
 
   char* st0 = smem;
   char* st1 = smem + kStageBytes;
@@ -272,29 +350,32 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     const int n = min(kGroup, min(B - cg * kGroup, kv_end - key0));
     if (++cg == upp) { cg = 0; ++cp; }
     const uint32_t sbase = lds_addr(st);
+    const int hk0 = key0 + kHalfKeys * kh;   // first key of this wave's half
+    // The half holds no live key, or (causal) every key of it lies after
+    // the wave's last row: nothing to add.
+    const bool active = wave_rows > 0 && kHalfKeys * kh < n && !(a.causal && hk0 > wave_last_pos);
 
-    // S^T = K Q^T: key block kb (16 keys) in s[kb].  LDS reads run one
-    // d-step ahead of the MFMAs.
-    f32x4 s[4];
+    // S^T = K Q^T: key block kb (16 keys), row block rb in s[kb][rb].  LDS
+    // reads run one d-step ahead of the MFMAs; each read feeds two MFMAs.
+    f32x4 s[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb) s[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    {
-      const uint32_t k0a = sbase + k_t[0], k1a = sbase + k_t[1], k2a = sbase + k_t[2], k3a = sbase + k_t[3];
-      u32x4 kv[2][4];
-      // d-step ds: base k_t[ds & 3], immediate kb * 8192 + (ds >> 2) * 256
-      auto kread = [&](int ds, u32x4 (&d)[4]) {
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (active) {
+      const uint32_t kbase = sbase + k_lane;
+      u32x4 kv[2][2];
+      // d-step ds: address kbase ^ ((ds & 3) << 6), immediate kb * 8192 + (ds >> 2) * 256
+      auto kread = [&](int ds, u32x4 (&d)[2]) {
         switch (ds) {
-#define PA_KB(DS) (((DS) & 3) == 0 ? k0a : ((DS) & 3) == 1 ? k1a : ((DS) & 3) == 2 ? k2a : k3a)
 #define PA_KR(DS)                                                                  \
-  case DS:                                                                         \
-    PA_DS_READ_B128(d[0], PA_KB(DS), 0 * 8192 + ((DS) >> 2) * 256);                \
-    PA_DS_READ_B128(d[1], PA_KB(DS), 1 * 8192 + ((DS) >> 2) * 256);                \
-    PA_DS_READ_B128(d[2], PA_KB(DS), 2 * 8192 + ((DS) >> 2) * 256);                \
-    PA_DS_READ_B128(d[3], PA_KB(DS), 3 * 8192 + ((DS) >> 2) * 256);                \
-    break;
+  case DS: {                                                                       \
+    const uint32_t ad = kbase ^ (((DS) & 3) << 6);                                 \
+    PA_DS_READ_B128(d[0], ad, 0 * 8192 + ((DS) >> 2) * 256);                       \
+    PA_DS_READ_B128(d[1], ad, 1 * 8192 + ((DS) >> 2) * 256);                       \
+  } break;
           PA_KR(0) PA_KR(1) PA_KR(2) PA_KR(3) PA_KR(4) PA_KR(5) PA_KR(6) PA_KR(7)
 #undef PA_KR
-#undef PA_KB
         }
       };
       kread(0, kv[0]);
@@ -303,91 +384,94 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         const int cur = ds & 1;
         if (ds < 7) {
           kread(ds + 1, kv[cur ^ 1]);
-          asm volatile("s_waitcnt lgkmcnt(4)"
-                       : "+v"(kv[cur][0]), "+v"(kv[cur][1]), "+v"(kv[cur][2]), "+v"(kv[cur][3]));
+          asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(kv[cur][0]), "+v"(kv[cur][1]));
         } else {
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(kv[cur][0]), "+v"(kv[cur][1]), "+v"(kv[cur][2]), "+v"(kv[cur][3]));
+          asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(kv[cur][0]), "+v"(kv[cur][1]));
         }
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) s[kb] = mfma16(kv[cur][kb], qb[ds], s[kb]);
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16(kv[cur][kb], qb[rb][ds], s[kb][rb]);
       }
     }
     if (more && w >= 4) issue(nst);
+    if (!active) continue;
 
-    // Soft-max.  s[kb][r] is key key0 + 16*kb + 4*kq + r of query row c16.
-    float sv[4][4];
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) sv[kb][r] = s[kb][r] * a.scale_log2;
-    const bool need_mask = (n < kGroup) || (a.causal && key0 + kGroup - 1 > wave_first_pos);
+    // Soft-max.  s[kb][rb][r] is key hk0 + 16*kb + 4*kq + r of query row
+    // 16*rb + c16; scores stay unscaled until the exponent (one fma).
+    const bool need_mask = (kHalfKeys * kh + kHalfKeys > n) || (a.causal && hk0 + kHalfKeys - 1 > wave_first_pos);
     if (need_mask) {
-      // key key0 + 16*kb + 4*kq + r is allowed iff it is below the group's
-      // live rows and (causal) at most my_pos
-      const int lim = a.causal ? min(n, my_pos - key0 + 1) : n;
-      const int lim_lane = lim - 4 * kq;
+      // key hk0 + 16*kb + 4*kq + r is allowed iff it is below the group's
+      // live rows and (causal) at most the row's position
+      const int ln = lane_here();
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int rb = 0; rb < 2; ++rb) {
+        const int row_pos = wave_first_pos + 16 * rb + (ln & 15);
+        const int lim = a.causal ? min(n, row_pos - key0 + 1) : n;
+        const int lim_lane = lim - kHalfKeys * kh - 4 * (ln >> 4);
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (16 * kb + r >= lim_lane) sv[kb][r] = -INFINITY;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            if (16 * kb + r >= lim_lane) s[kb][rb][r] = -INFINITY;
+      }
     }
-    float mx = sv[0][0];
+    // Lane maxima; only when one exceeds its row's threshold are the row
+    // maxima formed (two lane swaps) and the accumulators re-based.
+    float lm[2];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int rb = 0; rb < 2; ++rb)
+      lm[rb] = vmax(vmax3(vmax3(s[0][rb][0], s[0][rb][1], s[0][rb][2]), s[0][rb][3], s[1][rb][0]),
+                    vmax3(s[1][rb][1], s[1][rb][2], s[1][rb][3]));
+    // A raw score above (m_run + slack) / (scale log2 e) needs re-basing.
+    const float thr0 = fmaf(m_run[0], a.inv_scale_log2, kRescaleSlack * a.inv_scale_log2);
+    const float thr1 = fmaf(m_run[1], a.inv_scale_log2, kRescaleSlack * a.inv_scale_log2);
+    if (__any(lm[0] > thr0 || lm[1] > thr1)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sv[kb][r]);
-    mx = pair32_max(pair16_max(mx));
-    if (__any(mx > m_run + kRescaleSlack)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : fast_exp2(m_run - m_new);
+      for (int rb = 0; rb < 2; ++rb) {
+        const float mx = pair32_max(pair16_max(lm[rb])) * a.scale_log2;
+        const float m_new = fmaxf(m_run[rb], mx);
+        const float alpha = fast_exp2(m_run[rb] - m_new);
 #pragma unroll
-      for (int db = 0; db < 16; ++db) o[db] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
+        for (int db = 0; db < 16; ++db) o[db][rb] *= alpha;
+        l_run[rb] *= alpha;
+        m_run[rb] = m_new;
+      }
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
-    // P^T operand of key step ks: k = 0..3 <- block 2*ks, k = 4..7 <- block
-    // 2*ks + 1 (registers r = 0..3), packed to bf16
     u32x4 pb[2];
-    float rs = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
+    for (int rb = 0; rb < 2; ++rb) {
+      // P^T operand: k = 0..3 <- key block 0, k = 4..7 <- key block 1
+      // (registers r = 0..3), packed to bf16
       float p[8];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        p[r] = fast_exp2(sv[2 * ks][r] - m_use);
-        p[4 + r] = fast_exp2(sv[2 * ks + 1][r] - m_use);
+        p[r] = fast_exp2(fmaf(s[0][rb][r], a.scale_log2, -m_run[rb]));
+        p[4 + r] = fast_exp2(fmaf(s[1][rb][r], a.scale_log2, -m_run[rb]));
       }
-      rs += ((p[0] + p[1]) + (p[2] + p[3])) + ((p[4] + p[5]) + (p[6] + p[7]));
-      pb[ks] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
+      pb[rb] = u32x4{pack_bf16x2(p[0], p[1]), pack_bf16x2(p[2], p[3]),
                      pack_bf16x2(p[4], p[5]), pack_bf16x2(p[6], p[7])};
-    }
-    l_run += rs;
-
-    // O^T += V^T P^T: d-block db, key step ks.  The reads of a batch (four
-    // d-blocks, one key step) run one batch ahead of its MFMAs.
-    {
-      uint32_t wv[8];
+      // row sum of the rounded P (the values PV multiplies), two at a time
 #pragma unroll
-      for (int t = 0; t < 8; ++t) wv[t] = sbase + v_t[t];
-      u32x2 va[2][4][2];
-      // batch b = 2*dg + ks: d-blocks 4*dg .. 4*dg+3 (bases v_t[4*(dg & 1) + t],
-      // immediate 256*(dg >> 1)), keys 32*ks + 4*kq (immediate 32*ks*512) and
-      // + 16 (another 16*512)
-      auto vread = [&](int b, u32x2 (&d)[4][2]) {
+      for (int j = 0; j < 4; ++j) l_run[rb] = dot2_ones(pb[rb][j], l_run[rb]);
+    }
+
+    // O^T += V^T P^T: d-block db, both row blocks.  The reads of a batch
+    // (two d-blocks) run one batch ahead of its MFMAs.
+    {
+      const uint32_t vbase = sbase + v_lane;
+      u32x2 va[2][2][2];
+      // batch b: d-blocks 2*b, 2*b + 1
+      auto vread = [&](int b, u32x2 (&d)[2][2]) {
         switch (b) {
 #define PA_VR(BB)                                                                        \
   case BB: {                                                                             \
-    constexpr int dg = (BB) >> 1;                                                        \
-    constexpr int off0 = 256 * (dg >> 1) + 32 * ((BB) & 1) * kRowBytes;                  \
-    constexpr int off1 = off0 + 16 * kRowBytes;                                          \
-    constexpr int tb = 4 * (dg & 1);                                                     \
-    PA_DS_READ_TR16(d[0][0], wv[tb + 0], off0); PA_DS_READ_TR16(d[0][1], wv[tb + 0], off1); \
-    PA_DS_READ_TR16(d[1][0], wv[tb + 1], off0); PA_DS_READ_TR16(d[1][1], wv[tb + 1], off1); \
-    PA_DS_READ_TR16(d[2][0], wv[tb + 2], off0); PA_DS_READ_TR16(d[2][1], wv[tb + 2], off1); \
-    PA_DS_READ_TR16(d[3][0], wv[tb + 3], off0); PA_DS_READ_TR16(d[3][1], wv[tb + 3], off1); \
+    constexpr int db0 = 2 * (BB), db1 = 2 * (BB) + 1;                                    \
+    const uint32_t a0 = vbase ^ ((db0 & 7) << 5), a1 = vbase ^ ((db1 & 7) << 5);         \
+    PA_DS_READ_TR16(d[0][0], a0, 256 * (db0 >> 3));                                      \
+    PA_DS_READ_TR16(d[0][1], a0, 256 * (db0 >> 3) + 16 * kRowBytes);                     \
+    PA_DS_READ_TR16(d[1][0], a1, 256 * (db1 >> 3));                                      \
+    PA_DS_READ_TR16(d[1][1], a1, 256 * (db1 >> 3) + 16 * kRowBytes);                     \
   } break;
           PA_VR(0) PA_VR(1) PA_VR(2) PA_VR(3) PA_VR(4) PA_VR(5) PA_VR(6) PA_VR(7)
 #undef PA_VR
@@ -399,37 +483,78 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         const int cur = b & 1;
         if (b < 7) {
           vread(b + 1, va[cur ^ 1]);
-          asm volatile("s_waitcnt lgkmcnt(8)"
-                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]),
-                         "+v"(va[cur][2][0]), "+v"(va[cur][2][1]), "+v"(va[cur][3][0]), "+v"(va[cur][3][1]));
+          asm volatile("s_waitcnt lgkmcnt(4)"
+                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
         } else {
           asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]),
-                         "+v"(va[cur][2][0]), "+v"(va[cur][2][1]), "+v"(va[cur][3][0]), "+v"(va[cur][3][1]));
+                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
         }
-        const int dg = b >> 1, ks = b & 1;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          // d-block 4*dg + t
+        for (int t = 0; t < 2; ++t) {
           const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
-          o[4 * dg + t] = mfma16(av, pb[ks], o[4 * dg + t]);
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pb[rb], o[2 * b + t][rb]);
         }
       }
     }
   }
 
-  // Row sum over the four lanes of the row, then normalize and store:
-  // lane (kq, c16) holds d = 16*db + 4*kq + r of query row c16.
-  const float l_tot = pair32_sum(pair16_sum(l_run));
-  const float inv = 1.f / l_tot;
-  if (row_ok) {
-    uint16_t* op = a.out + (int64_t)my_row * q_stride + head * kHeadDim + 4 * kq;
+  // Merge the two key halves of every row, then normalize and store.  Lane
+  // (kq, c16) holds d = 16*db + 4*kq + r of query row 16*rb + c16; wave w
+  // finishes d-blocks 8*kh .. 8*kh+7 and hands its partner (w ^ 4) the
+  // other eight.  Lane-derived values are recomputed here rather than kept
+  // in registers across the loop.
+  const int lane_e = __lane_id();
+  float l_tot[2];
 #pragma unroll
-    for (int db = 0; db < 16; ++db) {
-      const u32x2 v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
-      *reinterpret_cast<u32x2*>(op + 16 * db) = v;
+  for (int rb = 0; rb < 2; ++rb) l_tot[rb] = pair32_sum(pair16_sum(l_run[rb]));
+  __syncthreads();   // every wave is done with the stages
+  f32x4* xo_mine = reinterpret_cast<f32x4*>(smem + w * kXoWaveBytes);
+  const f32x4* xo_peer = reinterpret_cast<const f32x4*>(smem + (w ^ 1) * kXoWaveBytes);
+  float* ml_mine = reinterpret_cast<float*>(smem + kMlOff + w * (2 * 64 * 8));
+  const float* ml_peer = reinterpret_cast<const float*>(smem + kMlOff + (w ^ 1) * (2 * 64 * 8));
+  // d-blocks 8*mine .. 8*mine+7 are this wave's; the half index is a
+  // template constant so the accumulator stays in registers.
+  auto hand_off = [&](auto half_tag) {
+    constexpr int other = 1 - decltype(half_tag)::value;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) xo_mine[(rb * 8 + j) * 64 + lane_e] = o[8 * other + j][rb];
+      ml_mine[(rb * 64 + lane_e) * 2] = m_run[rb];
+      ml_mine[(rb * 64 + lane_e) * 2 + 1] = l_tot[rb];
     }
-  }
+  };
+  auto finish = [&](auto half_tag) {
+    constexpr int mine = decltype(half_tag)::value;
+#pragma unroll
+    for (int rb = 0; rb < 2; ++rb) {
+      const float mp = ml_peer[(rb * 64 + lane_e) * 2];
+      const float lp = ml_peer[(rb * 64 + lane_e) * 2 + 1];
+      const float M = fmaxf(m_run[rb], mp);
+      const float f = fast_exp2(m_run[rb] - M);
+      const float fp = fast_exp2(mp - M);
+      const float inv = 1.f / (f * l_tot[rb] + fp * lp);
+      const float fa = f * inv, fb = fp * inv;
+      const int row = wrow0 + 16 * rb + (lane_e & 15);
+      if (row < a.q_len) {
+        uint16_t* op = a.out + (int64_t)row * q_stride + head * kHeadDim + 4 * (lane_e >> 4);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const f32x4 x = o[8 * mine + j][rb];
+          const f32x4 y = xo_peer[(rb * 8 + j) * 64 + lane_e];
+          const u32x2 v = {pack_bf16x2(x[0] * fa + y[0] * fb, x[1] * fa + y[1] * fb),
+                           pack_bf16x2(x[2] * fa + y[2] * fb, x[3] * fa + y[3] * fb)};
+          *reinterpret_cast<u32x2*>(op + 16 * (8 * mine + j)) = v;
+        }
+      }
+    }
+  };
+  if (kh == 0) hand_off(std::integral_constant<int, 0>{});
+  else hand_off(std::integral_constant<int, 1>{});
+  __syncthreads();
+  if (kh == 0) finish(std::integral_constant<int, 0>{});
+  else finish(std::integral_constant<int, 1>{});
 }
 
 }  // namespace
@@ -450,6 +575,7 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   a.causal = causal ? 1 : 0;
   a.block_size = block_size;
   a.scale_log2 = scale * 1.4426950408889634f;
+  a.inv_scale_log2 = 1.f / a.scale_log2;
   a.num_kv_heads = num_kv_heads;
   a.num_q_tiles = (q_len + kBM - 1) / kBM;
   hipLaunchKernelGGL(prefill_kernel, dim3(num_kv_heads * kGqa * a.num_q_tiles), dim3(kWavesPf * 64),

@@ -78,6 +78,10 @@ def test_decode_validation():
     assert _decode(q=FAKE_MIS) == C["PA_ERR_ALIGN"]
     assert _decode(k=FAKE_MIS) == C["PA_ERR_ALIGN"]
     assert _decode(ws=None) == C["PA_ERR_WORKSPACE"]
+    assert _decode(scale=0.0) == C["PA_ERR_SCALE"]
+    assert _decode(scale=-0.0625) == C["PA_ERR_SCALE"]
+    assert _decode(scale=float("inf")) == C["PA_ERR_SCALE"]
+    assert _decode(scale=float("nan")) == C["PA_ERR_SCALE"]
     need = pa.decode_workspace_size(1, 8193, 832, 4)
     assert _decode(ws_bytes=need - 1) == C["PA_ERR_WORKSPACE"]
 
@@ -103,6 +107,7 @@ def test_decode_append_validation():
     assert _append(d=128) == C["PA_ERR_UNSUPPORTED"]
     assert _append(bt_stride=9) == C["PA_ERR_TABLE"]
     assert _append(ws=None) == C["PA_ERR_WORKSPACE"]
+    assert _append(scale=-1.0) == C["PA_ERR_SCALE"]
     need = pa.decode_workspace_size(1, 8193, 832, 4)
     assert _append(ws_bytes=need - 1) == C["PA_ERR_WORKSPACE"]
 
@@ -139,6 +144,9 @@ def test_prefill_validation():
     assert _prefill(n_bt=9) == C["PA_ERR_TABLE"]               # 9 * 832 < 8192
     assert _prefill(page_stride=100) == C["PA_ERR_STRIDE"]
     assert _prefill(out=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    assert _prefill(scale=0.0) == C["PA_ERR_SCALE"]
+    assert _prefill(scale=-0.0625) == C["PA_ERR_SCALE"]
+    assert _prefill(scale=float("nan")) == C["PA_ERR_SCALE"]
 
 
 def test_kv_write_and_slot_mapping_validation():
