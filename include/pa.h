@@ -13,7 +13,8 @@
  * Conventions shared by every call
  *  - Every pointer argument is a DEVICE pointer (memory the caller allocated
  *    with hipMalloc or a framework on top of it), except the size_t* outputs
- *    of pa_decode_workspace_size, which are host pointers.
+ *    of pa_decode_workspace_size and the int32_t* output of
+ *    pa_page_size_for_hybrid, which are host pointers.
  *  - bf16 tensors are passed as uint16_t* holding bf16 bit patterns.  All
  *    bf16 tensors must be 16-byte aligned.
  *  - KV cache layout ([ALIGN] §4): K and V are separate tensors, each
@@ -209,6 +210,26 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                      int64_t page_stride, const int32_t* block_table, int32_t num_table_entries,
                      int32_t block_size, float scale, int32_t num_q_heads, int32_t num_kv_heads,
                      int32_t head_dim, void* stream);
+
+/*
+ * KV page size (tokens) of a hybrid attention / Mamba-state model ([ALIGN]
+ * §3): the attention page must hold at least one Mamba state page, in whole
+ * groups of alignment_tokens tokens,
+ *   block_size = ceil(mamba_page_bytes /
+ *                     (alignment_tokens * attn_page_bytes_per_token))
+ *                * alignment_tokens,
+ * the abstraction the page prints (its minimum comparison and later padding
+ * branches are left out).  attn_page_bytes_per_token is one token's K and V
+ * of one attention layer: 2 * num_kv_heads * head_dim * sizeof(element), 4096
+ * bytes for 4 KV heads of 256 bf16 values ([ALIGN] §4).  With alignment 16 a
+ * Mamba page in (3 145 728, 3 211 264] bytes gives 784 tokens, with alignment
+ * 64 (the wave64 access group, [ALIGN] §2) 832.  Host-only arithmetic, no
+ * device work; block_size_out is a host pointer.
+ * Errors: PA_ERR_NULL, PA_ERR_SIZE (an argument <= 0, or a result above
+ * 2^31 - 1).
+ */
+int pa_page_size_for_hybrid(int64_t mamba_page_bytes, int64_t attn_page_bytes_per_token,
+                            int32_t alignment_tokens, int32_t* block_size_out);
 
 /* Static string naming an error code (never NULL). */
 const char* pa_strerror(int code);

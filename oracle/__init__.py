@@ -26,4 +26,10 @@ from .paged_attention import (  # noqa: F401
     decode,
     prefill_chunk,
 )
-from .page_geometry import groups_in_page, page_bytes, smallest_aligned_page  # noqa: F401
+from .page_geometry import (  # noqa: F401
+    attn_page_bytes_per_token,
+    groups_in_page,
+    page_bytes,
+    required_page_tokens,
+    smallest_aligned_page,
+)

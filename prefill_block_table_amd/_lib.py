@@ -31,6 +31,8 @@ lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp
 for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
            "pa_decode", "pa_decode_append", "pa_prefill_chunk"):
     getattr(lib, _f).restype = ctypes.c_int
+lib.pa_page_size_for_hybrid.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_i32)]
+lib.pa_page_size_for_hybrid.restype = ctypes.c_int
 lib.pa_strerror.argtypes = [ctypes.c_int]
 lib.pa_strerror.restype = ctypes.c_char_p
 lib.pa_build_info.argtypes = []
@@ -163,6 +165,17 @@ def decode_workspace_size(num_seqs: int, max_seq_len: int, block_size: int,
                                         int(num_kv_heads), ctypes.byref(n)),
            "pa_decode_workspace_size")
     return n.value
+
+
+def page_size_for_hybrid(mamba_page_bytes: int, attn_page_bytes_per_token: int = 4096,
+                         alignment_tokens: int = 64) -> int:
+    """KV page size in tokens for a hybrid attention / Mamba model (see
+    pa_page_size_for_hybrid in include/pa.h)."""
+    out = ctypes.c_int32(0)
+    _check(lib.pa_page_size_for_hybrid(int(mamba_page_bytes), int(attn_page_bytes_per_token),
+                                       int(alignment_tokens), ctypes.byref(out)),
+           "pa_page_size_for_hybrid")
+    return out.value
 
 
 def decode_workspace(num_seqs: int, max_seq_len: int, block_size: int, num_kv_heads: int = 4,

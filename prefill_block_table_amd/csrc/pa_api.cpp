@@ -195,6 +195,20 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                                           num_kv_heads, static_cast<hipStream_t>(stream)));
 }
 
+int pa_page_size_for_hybrid(int64_t mamba_page_bytes, int64_t attn_page_bytes_per_token,
+                            int32_t alignment_tokens, int32_t* block_size_out) {
+  if (!block_size_out) return PA_ERR_NULL;
+  if (mamba_page_bytes <= 0 || attn_page_bytes_per_token <= 0 || alignment_tokens <= 0)
+    return PA_ERR_SIZE;
+  // bytes of one alignment group of attention tokens; quotient rounded up
+  if (attn_page_bytes_per_token > INT64_MAX / alignment_tokens) return PA_ERR_SIZE;
+  const int64_t group_bytes = attn_page_bytes_per_token * alignment_tokens;
+  const int64_t groups = mamba_page_bytes / group_bytes + (mamba_page_bytes % group_bytes != 0);
+  if (groups > INT32_MAX / alignment_tokens) return PA_ERR_SIZE;
+  *block_size_out = (int32_t)(groups * alignment_tokens);
+  return PA_OK;
+}
+
 const char* pa_strerror(int code) {
   switch (code) {
     case PA_OK: return "ok";

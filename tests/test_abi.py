@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused",
                           "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
-                          "pa_prefill_chunk",
+                          "pa_prefill_chunk", "pa_page_size_for_hybrid",
                           "pa_strerror", "pa_build_info"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True).stdout

@@ -491,3 +491,44 @@ def test_oracle_rejects_empty():
         oracle.prefill_chunk(np.zeros((0, 24, 8), np.uint16), 0, True,
                              np.zeros((1, 4, 4, 8), np.uint16), np.zeros((1, 4, 4, 8), np.uint16),
                              np.array([0], np.int32), 4, 1.0)
+
+
+# ---- page-size derivation (page-alignment post, section 3) -------------------
+
+def _page_facts():
+    return json.load(open(os.path.join(GOLDEN, "page_facts.json")))
+
+
+def test_page_derivation_reproduces_printed_pages():
+    """784 at the generic alignment, 832 at the backend's 64, for every Mamba
+    page size the printed pair allows (section 3), with the section 4 shape."""
+    g = _page_facts()["page_derivation"]
+    per_tok = oracle.attn_page_bytes_per_token(4, 256, 2)
+    assert per_tok == 4096
+    lo, hi = 48 * 16 * per_tok, 49 * 16 * per_tok          # (3145728, 3211264]
+    for m in (lo + 1, lo + 4096, (lo + hi) // 2, hi - 1, hi):
+        assert oracle.required_page_tokens(m, per_tok, g["alignment_generic"]) == g["default_page_generic"]
+        assert oracle.required_page_tokens(m, per_tok, g["alignment_backend"]) == g["page_backend"]
+    # just outside the range the generic page moves off 784
+    assert oracle.required_page_tokens(lo, per_tok, 16) == 768
+    assert oracle.required_page_tokens(hi + 1, per_tok, 16) == 800
+
+
+def test_page_derivation_brute_force():
+    """The result is the smallest multiple of the alignment whose attention
+    page holds at least one Mamba page: checked by scanning multiples."""
+    rng = np.random.Generator(np.random.PCG64(11))
+    for _ in range(300):
+        per_tok = int(rng.integers(1, 9000))
+        align = int(rng.choice([1, 3, 16, 64, 128]))
+        m = int(rng.integers(1, 5_000_000))
+        tokens = align
+        while tokens * per_tok < m:
+            tokens += align
+        assert oracle.required_page_tokens(m, per_tok, align) == tokens
+
+
+def test_page_derivation_rejects_nonpositive():
+    for args in ((0, 4096, 64), (1000, 0, 64), (1000, 4096, 0), (-5, 4096, 64)):
+        with pytest.raises(ValueError):
+            oracle.required_page_tokens(*args)
