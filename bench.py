@@ -240,6 +240,42 @@ def bench_prefill(D, pa, case, steps, warmup):
     return out
 
 
+def bench_input_prep(D, pa, iters=2000, warmup=100):
+    """Single-token decode input preparation at the input-prep post's
+    benchmark configuration (position 24576, two KV groups of page 16, 128
+    request slots, 4096 token slots, M-RoPE): device time per launch of
+    back-to-back launches, and host time per call through the binding."""
+    torch = D.torch
+    np = D.np
+    P, R, N, Bs = 24576, 128, 4096, [16, 16]
+    dev = "cuda"
+    sampled = torch.tensor([151_643], dtype=torch.int64, device=dev)
+    ids = torch.zeros(N, dtype=torch.int32, device=dev)
+    pos = torch.zeros(3, N + 1, dtype=torch.int64, device=dev)
+    qsl = torch.zeros(R + 1, dtype=torch.int32, device=dev)
+    sl = torch.zeros(R, dtype=torch.int32, device=dev)
+    mask = torch.ones(R, dtype=torch.bool, device=dev)
+    rng = np.random.Generator(np.random.PCG64(24576))
+    tables = [torch.from_numpy(rng.permutation(1 << 16)[:2048].astype(np.int32)).to(dev) for _ in Bs]
+    slots = [torch.zeros(N, dtype=torch.int64, device=dev) for _ in Bs]
+    bs = torch.tensor(Bs, dtype=torch.int32, device=dev)
+    btp = torch.tensor([t.data_ptr() for t in tables], dtype=torch.int64, device=dev)
+    smp = torch.tensor([t.data_ptr() for t in slots], dtype=torch.int64, device=dev)
+
+    def step(i, ev=None):
+        pa.decode_input_prep(sampled, P, ids, pos, qsl, sl, mask, block_sizes=bs,
+                             block_table_ptrs=btp, slot_mapping_ptrs=smp, mrope=True)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    total_ms, _, host_s = timed_loop(torch, iters, step, 0.02 * iters + 20, events=False)
+    return {"config": "position 24576, 2 KV groups of page 16, 128 request slots, 4096 token "
+                      "slots, M-RoPE", "launches": iters,
+            "device_us_per_launch": total_ms / iters * 1e3,
+            "host_us_per_call": host_s / iters * 1e6}
+
+
 def decode_src_sha():
     import hashlib
     with open(DECODE_SRC, "rb") as f:
@@ -363,6 +399,8 @@ def main():
         extra["decode_batch16_ctx4k_32k_b832"] = bench_decode(D, pa, W.batched_decode(),
                                                               max(20, args.steps // 4),
                                                               args.warmup, rotate=True)
+        print("[bench] decode input prep", file=sys.stderr, flush=True)
+        extra["decode_input_prep"] = bench_input_prep(D, pa)
         print("[bench] prefill", file=sys.stderr, flush=True)
         extra["prefill_b832"] = bench_prefill(D, pa, W.prefill_8k(), max(10, args.steps // 5),
                                               min(args.warmup, 5))

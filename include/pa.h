@@ -212,6 +212,42 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                      int32_t head_dim, void* stream);
 
 /*
+ * Model inputs and attention metadata of one single-request, single-token
+ * decode step, written by one launch ([PREP] §2: when one request advances
+ * by one token every entry is a closed form; §4, §5: the sampled token stays
+ * on the device and one launch, one workgroup per KV-cache group, writes
+ * everything; §3.2: the slot formula).  Writes
+ *   input_ids[0]           = (int32) sampled_token_ids[0]
+ *   positions[0]           = position                       (mrope == 0)
+ *   positions[r * positions_stride] = position + mrope_delta,  r = 0, 1, 2
+ *                                                            (mrope != 0)
+ *   query_start_loc[0 .. query_start_loc_len) = 0, 1, 1, ..., 1
+ *   seq_lens[0 .. seq_lens_len)               = position + 1, 0, ..., 0
+ *   discard_request_mask[0 .. discard_len)    = 0 (false)
+ *   is_token_ids[0]        = 1                               (if not NULL)
+ *   for each KV-cache group g < num_kv_groups, with B = block_sizes[g],
+ *   bt = (const int32_t*) block_table_ptrs[g] (the request's block-table
+ *   row) and sm = (int64_t*) slot_mapping_ptrs[g]:
+ *     sm[0] = bt[position / B] * B + position % B   (-1 when B <= 0)
+ * and nothing else.  Every pointer, and every address inside the two
+ * uint64 arrays, is a device address; block_sizes, block_table_ptrs and
+ * slot_mapping_ptrs may be NULL when num_kv_groups == 0.  position is the
+ * number of tokens already computed (the new token's index); position / B
+ * must index a valid entry of each group's row (not checked).
+ * Errors: PA_ERR_NULL, PA_ERR_SIZE (position < 0 or >= 2^31 - 1,
+ * query_start_loc_len < 2, seq_lens_len < 1, discard_len < 1, num_kv_groups
+ * outside [0, 65535], mrope with positions_stride < 1), PA_ERR_LAUNCH.
+ */
+int pa_decode_input_prep(const int64_t* sampled_token_ids, int64_t position, int32_t* input_ids,
+                         int64_t* positions, int32_t mrope, int64_t positions_stride,
+                         int64_t mrope_delta, int32_t* query_start_loc,
+                         int32_t query_start_loc_len, int32_t* seq_lens, int32_t seq_lens_len,
+                         uint8_t* discard_request_mask, int32_t discard_len,
+                         uint8_t* is_token_ids, int32_t num_kv_groups, const int32_t* block_sizes,
+                         const uint64_t* block_table_ptrs, const uint64_t* slot_mapping_ptrs,
+                         void* stream);
+
+/*
  * KV page size (tokens) of a hybrid attention / Mamba-state model ([ALIGN]
  * §3): the attention page must hold at least one Mamba state page, in whole
  * groups of alignment_tokens tokens,

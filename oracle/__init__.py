@@ -26,6 +26,7 @@ from .paged_attention import (  # noqa: F401
     decode,
     prefill_chunk,
 )
+from .input_prep import decode_input_prep  # noqa: F401
 from .page_geometry import (  # noqa: F401
     attn_page_bytes_per_token,
     groups_in_page,

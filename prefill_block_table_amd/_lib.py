@@ -31,6 +31,9 @@ lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp
 for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
            "pa_decode", "pa_decode_append", "pa_prefill_chunk"):
     getattr(lib, _f).restype = ctypes.c_int
+lib.pa_decode_input_prep.argtypes = [_vp, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32,
+                                     _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]
+lib.pa_decode_input_prep.restype = ctypes.c_int
 lib.pa_page_size_for_hybrid.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_i32)]
 lib.pa_page_size_for_hybrid.restype = ctypes.c_int
 lib.pa_strerror.argtypes = [ctypes.c_int]
@@ -165,6 +168,48 @@ def decode_workspace_size(num_seqs: int, max_seq_len: int, block_size: int,
                                         int(num_kv_heads), ctypes.byref(n)),
            "pa_decode_workspace_size")
     return n.value
+
+
+def decode_input_prep(sampled_token_ids, position: int, input_ids, positions, query_start_loc,
+                      seq_lens, discard_request_mask, block_sizes=None, block_table_ptrs=None,
+                      slot_mapping_ptrs=None, mrope: bool = False, mrope_delta: int = 0,
+                      is_token_ids=None):
+    """One launch that writes a single-token decode step's inputs and metadata
+    (see pa_decode_input_prep in include/pa.h).
+
+    sampled_token_ids int64 [>=1]; input_ids int32; positions int64 ([N] or,
+    with mrope, [3, N]); query_start_loc, seq_lens int32; discard_request_mask
+    and is_token_ids bool or uint8; block_sizes int32 [G]; block_table_ptrs and
+    slot_mapping_ptrs uint64/int64 [G] holding device addresses (int32 rows,
+    int64 outputs).  All on the device.  Enqueued on the current stream."""
+    dev = input_ids.device
+    _need(sampled_token_ids, "sampled_token_ids", (torch.int64,), dev)
+    _need(input_ids, "input_ids", (torch.int32,), dev)
+    _need(positions, "positions", (torch.int64,), dev)
+    _need(query_start_loc, "query_start_loc", (torch.int32,), dev)
+    _need(seq_lens, "seq_lens", (torch.int32,), dev)
+    _need(discard_request_mask, "discard_request_mask", (torch.bool, torch.uint8), dev)
+    if is_token_ids is not None:
+        _need(is_token_ids, "is_token_ids", (torch.bool, torch.uint8), dev)
+    stride = 0
+    if mrope:
+        if positions.dim() != 2 or positions.shape[0] != 3:
+            raise ValueError("with mrope, positions must be [3, N]")
+        stride = positions.stride(0)
+    G = 0 if block_sizes is None else int(block_sizes.numel())
+    if G:
+        _need(block_sizes, "block_sizes", (torch.int32,), dev)
+        _need(block_table_ptrs, "block_table_ptrs", (torch.uint64, torch.int64), dev)
+        _need(slot_mapping_ptrs, "slot_mapping_ptrs", (torch.uint64, torch.int64), dev)
+        if block_table_ptrs.numel() < G or slot_mapping_ptrs.numel() < G:
+            raise ValueError("one block-table and one slot-mapping address per group")
+    _check(lib.pa_decode_input_prep(
+        _ptr(sampled_token_ids), int(position), _ptr(input_ids), _ptr(positions), int(bool(mrope)),
+        int(stride), int(mrope_delta), _ptr(query_start_loc), int(query_start_loc.numel()),
+        _ptr(seq_lens), int(seq_lens.numel()), _ptr(discard_request_mask),
+        int(discard_request_mask.numel()), _ptr(is_token_ids) if is_token_ids is not None else None,
+        G, _ptr(block_sizes) if G else None, _ptr(block_table_ptrs) if G else None,
+        _ptr(slot_mapping_ptrs) if G else None, _stream(input_ids)), "pa_decode_input_prep")
 
 
 def page_size_for_hybrid(mamba_page_bytes: int, attn_page_bytes_per_token: int = 4096,

@@ -195,6 +195,45 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                                           num_kv_heads, static_cast<hipStream_t>(stream)));
 }
 
+int pa_decode_input_prep(const int64_t* sampled_token_ids, int64_t position, int32_t* input_ids,
+                         int64_t* positions, int32_t mrope, int64_t positions_stride,
+                         int64_t mrope_delta, int32_t* query_start_loc,
+                         int32_t query_start_loc_len, int32_t* seq_lens, int32_t seq_lens_len,
+                         uint8_t* discard_request_mask, int32_t discard_len,
+                         uint8_t* is_token_ids, int32_t num_kv_groups, const int32_t* block_sizes,
+                         const uint64_t* block_table_ptrs, const uint64_t* slot_mapping_ptrs,
+                         void* stream) {
+  if (!sampled_token_ids || !input_ids || !positions || !query_start_loc || !seq_lens ||
+      !discard_request_mask)
+    return PA_ERR_NULL;
+  if (num_kv_groups < 0 || num_kv_groups > 65535) return PA_ERR_SIZE;
+  if (num_kv_groups > 0 && (!block_sizes || !block_table_ptrs || !slot_mapping_ptrs))
+    return PA_ERR_NULL;
+  if (position < 0 || position >= INT32_MAX) return PA_ERR_SIZE;
+  if (query_start_loc_len < 2 || seq_lens_len < 1 || discard_len < 1) return PA_ERR_SIZE;
+  if (mrope && positions_stride < 1) return PA_ERR_SIZE;
+  pa::InputPrepArgs a;
+  a.sampled_token_ids = sampled_token_ids;
+  a.position = position;
+  a.input_ids = input_ids;
+  a.positions = positions;
+  a.mrope = mrope ? 1 : 0;
+  a.positions_stride = positions_stride;
+  a.mrope_delta = mrope_delta;
+  a.query_start_loc = query_start_loc;
+  a.query_start_loc_len = query_start_loc_len;
+  a.seq_lens = seq_lens;
+  a.seq_lens_len = seq_lens_len;
+  a.discard_request_mask = discard_request_mask;
+  a.discard_len = discard_len;
+  a.is_token_ids = is_token_ids;
+  a.num_kv_groups = num_kv_groups;
+  a.block_sizes = block_sizes;
+  a.block_table_ptrs = block_table_ptrs;
+  a.slot_mapping_ptrs = slot_mapping_ptrs;
+  return launch_status(pa::launch_decode_input_prep(a, static_cast<hipStream_t>(stream)));
+}
+
 int pa_page_size_for_hybrid(int64_t mamba_page_bytes, int64_t attn_page_bytes_per_token,
                             int32_t alignment_tokens, int32_t* block_size_out) {
   if (!block_size_out) return PA_ERR_NULL;

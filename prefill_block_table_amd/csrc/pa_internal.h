@@ -66,6 +66,30 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
                           int64_t page_stride, const int32_t* block_table, int32_t block_size,
                           float scale, int32_t num_kv_heads, hipStream_t stream);
 
+// Single-token decode input preparation (pa_decode_input_prep).
+struct InputPrepArgs {
+  const int64_t* sampled_token_ids;
+  int64_t position;
+  int32_t* input_ids;
+  int64_t* positions;
+  int32_t mrope;
+  int64_t positions_stride;
+  int64_t mrope_delta;
+  int32_t* query_start_loc;
+  int32_t query_start_loc_len;
+  int32_t* seq_lens;
+  int32_t seq_lens_len;
+  uint8_t* discard_request_mask;
+  int32_t discard_len;
+  uint8_t* is_token_ids;           // NULL: not written
+  int32_t num_kv_groups;
+  const int32_t* block_sizes;
+  const uint64_t* block_table_ptrs;
+  const uint64_t* slot_mapping_ptrs;
+};
+
+hipError_t launch_decode_input_prep(const InputPrepArgs& a, hipStream_t stream);
+
 extern const char* const kDecodeVariant;
 extern const char* const kPrefillVariant;
 

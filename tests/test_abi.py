@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused",
                           "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
-                          "pa_prefill_chunk", "pa_page_size_for_hybrid",
+                          "pa_prefill_chunk", "pa_page_size_for_hybrid", "pa_decode_input_prep",
                           "pa_strerror", "pa_build_info"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True).stdout
@@ -167,3 +167,26 @@ def test_kv_write_and_slot_mapping_validation():
     assert L.pa_slot_mapping(FAKE, FAKE, None, 1, FAKE, 10, 0, None) == C["PA_ERR_BLOCK_SIZE"]
     assert L.pa_slot_mapping(FAKE, FAKE, None, -5, FAKE, 10, 832, None) == C["PA_ERR_SIZE"]
     assert L.pa_slot_mapping(FAKE, FAKE, None, 0, FAKE, 10, 832, None) == 0
+
+
+def test_decode_input_prep_validation():
+    L = pa.lib
+    def call(**kw):
+        a = dict(sampled=FAKE, pos=100, ids=FAKE, positions=FAKE, mrope=0, stride=0, delta=0,
+                 qsl=FAKE, qsl_len=17, sl=FAKE, sl_len=16, mask=FAKE, mask_len=16, itk=None,
+                 G=2, bs=FAKE, btp=FAKE, smp=FAKE)
+        a.update(kw)
+        return L.pa_decode_input_prep(a["sampled"], a["pos"], a["ids"], a["positions"], a["mrope"],
+                                      a["stride"], a["delta"], a["qsl"], a["qsl_len"], a["sl"],
+                                      a["sl_len"], a["mask"], a["mask_len"], a["itk"], a["G"],
+                                      a["bs"], a["btp"], a["smp"], None)
+    assert call(sampled=None) == C["PA_ERR_NULL"]
+    assert call(ids=None) == C["PA_ERR_NULL"]
+    assert call(mask=None) == C["PA_ERR_NULL"]
+    assert call(btp=None) == C["PA_ERR_NULL"]
+    assert call(pos=-1) == C["PA_ERR_SIZE"]
+    assert call(pos=2**31 - 1) == C["PA_ERR_SIZE"]
+    assert call(qsl_len=1) == C["PA_ERR_SIZE"]
+    assert call(sl_len=0) == C["PA_ERR_SIZE"]
+    assert call(G=-1) == C["PA_ERR_SIZE"]
+    assert call(mrope=1, stride=0) == C["PA_ERR_SIZE"]

@@ -107,3 +107,62 @@ def test_pins_catch_mutant(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"mutant {name} passed every pin"
+
+
+# ---- input preparation -------------------------------------------------------
+
+_orig_prep = oracle.decode_input_prep
+
+
+def _prep_mutant(edit):
+    def f(*args, **kw):
+        out = _orig_prep(*args, **kw)
+        edit(out, args, kw)
+        return out
+    return f
+
+
+def _seq_lens_no_plus_one(out, args, kw):
+    out["seq_lens"][0] -= 1
+
+
+def _qsl_running_index(out, args, kw):
+    out["query_start_loc"][:] = np.arange(len(out["query_start_loc"]))
+
+
+def _slot_next_page(out, args, kw):
+    pos = args[1]
+    for B, row, sm in zip(kw["block_sizes"], kw["block_tables"], out["slot_mappings"]):
+        sm[0] = int(row[pos // B + 1]) * B + pos % B
+
+
+def _mrope_first_row_only(out, args, kw):
+    if kw.get("mrope"):
+        out["positions"][1:, 0] = -7
+
+
+def _input_id_from_position(out, args, kw):
+    out["input_ids"][0] = args[1]
+
+
+PREP_MUTANTS = {
+    "seq_lens_no_plus_one": _seq_lens_no_plus_one,
+    "qsl_running_index": _qsl_running_index,
+    "slot_next_page": _slot_next_page,
+    "mrope_first_row_only": _mrope_first_row_only,
+    "input_id_from_position": _input_id_from_position,
+}
+PREP_PINS = [pins.test_input_prep_printed_closed_forms, pins.test_input_prep_slot_matches_gather,
+             pins.test_input_prep_mrope_offset_and_is_token_ids]
+
+
+@pytest.mark.parametrize("name", sorted(PREP_MUTANTS))
+def test_input_prep_pins_catch_mutant(name, monkeypatch):
+    monkeypatch.setattr(oracle, "decode_input_prep", _prep_mutant(PREP_MUTANTS[name]))
+    caught = 0
+    for call in PREP_PINS:
+        try:
+            call()
+        except (AssertionError, ValueError, IndexError):
+            caught += 1
+    assert caught >= 1, f"mutant {name} passed every pin"

@@ -532,3 +532,66 @@ def test_page_derivation_rejects_nonpositive():
     for args in ((0, 4096, 64), (1000, 0, 64), (1000, 4096, 0), (-5, 4096, 64)):
         with pytest.raises(ValueError):
             oracle.required_page_tokens(*args)
+
+
+# ---- single-token decode input preparation (input-prep post) -----------------
+
+def _prep_case(position, block_sizes, n_tokens=64, n_reqs=16, mrope=False, seed=0):
+    rng = np.random.Generator(np.random.PCG64(seed))
+    tables = [rng.permutation(4096)[: -(-(position + 1) // B) + 3].astype(np.int32) for B in block_sizes]
+    poison = -7
+    bufs = dict(
+        input_ids=np.full(n_tokens, poison, np.int32),
+        positions=np.full((3, n_tokens + 1) if mrope else n_tokens, poison, np.int64),
+        query_start_loc=np.full(n_reqs + 1, poison, np.int32),
+        seq_lens=np.full(n_reqs, poison, np.int32),
+        discard_request_mask=np.ones(n_reqs, np.uint8),
+    )
+    slots = [np.full(n_tokens, poison, np.int64) for _ in block_sizes]
+    return tables, bufs, slots
+
+
+def test_input_prep_printed_closed_forms():
+    """The pages' closed forms (section 2) at their benchmark configuration
+    (section 11: position 24576, two KV groups of page 16, 128 request slots)."""
+    f = json.load(open(os.path.join(GOLDEN, "input_prep_facts.json")))["benchmark_config"]
+    P = f["position"]
+    tables, bufs, slots = _prep_case(P, f["block_sizes"], n_tokens=f["max_num_tokens"],
+                                     n_reqs=f["max_num_reqs"], mrope=True)
+    out = oracle.decode_input_prep(np.array([151_643], np.int64), P, block_sizes=f["block_sizes"],
+                                   block_tables=tables, slot_mappings=slots, mrope=True, **bufs)
+    assert out["input_ids"][0] == 151_643 and np.all(out["input_ids"][1:] == -7)
+    assert np.all(out["positions"][:, 0] == P) and np.all(out["positions"][:, 1:] == -7)
+    assert out["query_start_loc"].tolist() == [0] + [1] * f["max_num_reqs"]
+    assert out["seq_lens"].tolist() == [P + 1] + [0] * (f["max_num_reqs"] - 1)
+    assert not out["discard_request_mask"].any()
+    for B, row, sm in zip(f["block_sizes"], tables, out["slot_mappings"]):
+        # section 3.2 at P = 24576, B = 16: logical block 1536, offset 0
+        assert sm[0] == int(row[1536]) * 16 and np.all(sm[1:] == -7)
+
+
+def test_input_prep_slot_matches_gather():
+    """Slot of each group = the cache row that a page-table walk reaches for
+    the position (brute force over a flattened pool), for pages 16/784/832."""
+    for seed, P in enumerate([0, 1, 783, 784, 831, 832, 8192, 24576, 32767]):
+        Bs = [16, 784, 832]
+        tables, bufs, slots = _prep_case(P, Bs, seed=seed)
+        out = oracle.decode_input_prep(np.array([5], np.int64), P, block_sizes=Bs,
+                                       block_tables=tables, slot_mappings=slots, **bufs)
+        for B, row, sm in zip(Bs, tables, out["slot_mappings"]):
+            # walk: tokens 0..P fill pages row[0], row[1], ... B at a time
+            page_idx, off = 0, 0
+            for _ in range(P):
+                off += 1
+                if off == B:
+                    page_idx, off = page_idx + 1, 0
+            assert sm[0] == int(row[page_idx]) * B + off
+
+
+def test_input_prep_mrope_offset_and_is_token_ids():
+    tables, bufs, slots = _prep_case(100, [16], mrope=True)
+    itk = np.zeros(64, np.uint8)
+    out = oracle.decode_input_prep(np.array([9], np.int64), 100, block_sizes=[16], block_tables=tables,
+                                   slot_mappings=slots, mrope=True, mrope_delta=-37, is_token_ids=itk, **bufs)
+    assert out["positions"][:, 0].tolist() == [63, 63, 63]
+    assert out["is_token_ids"][0] == 1 and not out["is_token_ids"][1:].any()
