@@ -210,18 +210,19 @@ def bench_prefill(D, pa, case, steps, warmup):
         pos = D.t(np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64))
         kn, vn, q = D.t(ch.k_new), D.t(ch.v_new), D.t(ch.q)
         o = torch.empty_like(q)
+        ws = pa.prefill_workspace(ch.q_len, ch.start_pos, case.block_size, device=D.dev)
         torch.cuda.synchronize()
         w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         w0.record()
         pa.kv_write_fused(k, v, kn, vn, pos, bt)
         w1.record()
         for _ in range(warmup):
-            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
+            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o, workspace=ws)
 
         def step(i, ev):
             if ev is not None:
                 ev[0].record()
-            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
+            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o, workspace=ws)
             if ev is not None:
                 ev[1].record()
 
@@ -330,8 +331,9 @@ def prefill_pass(D, pa, W):
         pa.kv_write_fused(k, v, D.t(ch.k_new), D.t(ch.v_new), pos, bt)
         q = D.t(ch.q)
         o = torch.empty_like(q)
+        ws = pa.prefill_workspace(ch.q_len, ch.start_pos, case.block_size, device=D.dev)
         for _ in range(5):
-            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o)
+            pa.prefill_chunk(q, k, v, bt, ch.start_pos, case.scale, causal=True, out=o, workspace=ws)
         torch.cuda.synchronize()
 
 

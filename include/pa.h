@@ -13,7 +13,8 @@
  * Conventions shared by every call
  *  - Every pointer argument is a DEVICE pointer (memory the caller allocated
  *    with hipMalloc or a framework on top of it), except the size_t* outputs
- *    of pa_decode_workspace_size and the int32_t* output of
+ *    of pa_decode_workspace_size / pa_prefill_workspace_size and the int32_t*
+ *    output of
  *    pa_page_size_for_hybrid, which are host pointers.
  *  - bf16 tensors are passed as uint16_t* holding bf16 bit patterns.  All
  *    bf16 tensors must be 16-byte aligned.
@@ -202,14 +203,35 @@ int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16
  *                ceil((start_pos + q_len) / block_size) <= num_table_entries.
  * q_len >= 1, start_pos >= 0, start_pos + q_len < 2^31.
  * scale          positive and finite.
+ * workspace      device buffer of >= pa_prefill_workspace_size(...) bytes for
+ *                this chunk shape, 256-byte aligned, contents arbitrary; NULL
+ *                allowed when that size is 0.  Items (query head x 128-row
+ *                tile) run one per workgroup, heaviest first; when their count
+ *                leaves the last round of 256 workgroups (one per CU)
+ *                incomplete, the items of that round are cut along their key
+ *                groups and a second launch combines the parts (fixed order:
+ *                results are bitwise repeatable).  The workspace holds those
+ *                partial results.  Calls sharing a workspace must not run
+ *                concurrently.
  * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE,
- * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
+ * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_WORKSPACE,
+ * PA_ERR_LAUNCH.
  */
 int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int32_t start_pos,
                      int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
                      int64_t page_stride, const int32_t* block_table, int32_t num_table_entries,
                      int32_t block_size, float scale, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, void* stream);
+                     int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Bytes of device workspace pa_prefill_chunk needs for this chunk shape (0
+ * when the chunk's items fill whole rounds of workgroups).  bytes_out: host
+ * pointer.  Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED,
+ * PA_ERR_SIZE.
+ */
+int pa_prefill_workspace_size(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              size_t* bytes_out);
 
 /*
  * Model inputs and attention metadata of one single-request, single-token

@@ -27,9 +27,10 @@ lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, 
 lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32,
                                  _f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
-                                 _f32, _i32, _i32, _i32, _vp]
+                                 _f32, _i32, _i32, _i32, _vp, _sz, _vp]
+lib.pa_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
-           "pa_decode", "pa_decode_append", "pa_prefill_chunk"):
+           "pa_decode", "pa_decode_append", "pa_prefill_chunk", "pa_prefill_workspace_size"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.pa_decode_input_prep.argtypes = [_vp, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32,
                                      _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]
@@ -293,9 +294,27 @@ def decode_append(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, 
     return out
 
 
+def prefill_workspace_size(q_len: int, start_pos: int, block_size: int, causal: bool = True,
+                           num_kv_heads: int = 4) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib.pa_prefill_workspace_size(int(q_len), int(start_pos), int(bool(causal)), int(block_size),
+                                         GQA * int(num_kv_heads), int(num_kv_heads), HEAD_DIM,
+                                         ctypes.byref(n)), "pa_prefill_workspace_size")
+    return n.value
+
+
+def prefill_workspace(q_len: int, start_pos: int, block_size: int, causal: bool = True,
+                      num_kv_heads: int = 4, device="cuda"):
+    """A workspace for pa_prefill_chunk of this chunk shape (None if it needs none)."""
+    n = prefill_workspace_size(q_len, start_pos, block_size, causal, num_kv_heads)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
 def prefill_chunk(q_chunk, k_cache, v_cache, block_table, start_pos: int, scale: float,
-                  causal: bool = True, out: torch.Tensor = None) -> torch.Tensor:
-    """q_chunk [q_len, 6*Hkv, 256] at positions start_pos.. -> out, same shape (bf16)."""
+                  causal: bool = True, out: torch.Tensor = None,
+                  workspace: torch.Tensor = None) -> torch.Tensor:
+    """q_chunk [q_len, 6*Hkv, 256] at positions start_pos.. -> out, same shape (bf16).
+    A workspace of the size prefill_workspace_size gives is allocated when none is passed."""
     P, B, H, stride = _cache_geometry(k_cache, v_cache)
     _need(q_chunk, "q_chunk", _BF16, k_cache.device)
     _need(block_table, "block_table", (torch.int32,), k_cache.device)
@@ -306,8 +325,11 @@ def prefill_chunk(q_chunk, k_cache, v_cache, block_table, start_pos: int, scale:
     if out is None:
         out = torch.empty_like(q_chunk)
     _need(out, "out", _BF16, k_cache.device)
+    if workspace is None:
+        workspace = prefill_workspace(q_len, start_pos, B, causal, H, device=k_cache.device)
+    ws_ptr, ws_bytes = (None, 0) if workspace is None else (_ptr(workspace), workspace.numel() * workspace.element_size())
     _check(lib.pa_prefill_chunk(_ptr(out), _ptr(q_chunk), q_len, int(start_pos), int(bool(causal)),
                                 _ptr(k_cache), _ptr(v_cache), stride, _ptr(bt), bt.numel(), B,
-                                float(scale), GQA * H, H, HEAD_DIM, _stream(q_chunk)),
+                                float(scale), GQA * H, H, HEAD_DIM, ws_ptr, ws_bytes, _stream(q_chunk)),
            "pa_prefill_chunk")
     return out

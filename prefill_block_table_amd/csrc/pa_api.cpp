@@ -173,26 +173,50 @@ int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16
                        head_dim, workspace, workspace_bytes, &append, stream);
 }
 
+static int check_prefill_shape(int32_t q_len, int32_t start_pos, int32_t block_size,
+                               int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim) {
+  if (block_size < 1) return PA_ERR_BLOCK_SIZE;
+  const int rc = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  if (q_len < 1 || start_pos < 0 || (int64_t)start_pos + q_len + block_size > INT32_MAX)
+    return PA_ERR_SIZE;
+  return PA_OK;
+}
+
+int pa_prefill_workspace_size(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size,
+                              int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                              size_t* bytes_out) {
+  if (!bytes_out) return PA_ERR_NULL;
+  const int rc = check_prefill_shape(q_len, start_pos, block_size, num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  *bytes_out = pa::plan_prefill(q_len, start_pos, causal ? 1 : 0, block_size, num_kv_heads).bytes;
+  return PA_OK;
+}
+
 int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int32_t start_pos,
                      int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
                      int64_t page_stride, const int32_t* block_table, int32_t num_table_entries,
                      int32_t block_size, float scale, int32_t num_q_heads, int32_t num_kv_heads,
-                     int32_t head_dim, void* stream) {
+                     int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream) {
   if (!out || !q_chunk || !block_table) return PA_ERR_NULL;
   if (!scale_ok(scale)) return PA_ERR_SCALE;
   int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
   if (rc) return rc;
-  rc = check_heads(num_q_heads, num_kv_heads, head_dim);
+  rc = check_prefill_shape(q_len, start_pos, block_size, num_q_heads, num_kv_heads, head_dim);
   if (rc) return rc;
-  if (q_len < 1 || start_pos < 0 || (int64_t)start_pos + q_len + block_size > INT32_MAX)
-    return PA_ERR_SIZE;
   const int64_t kv_len = (int64_t)start_pos + q_len;
   if (num_table_entries < 1 || (int64_t)num_table_entries * block_size < kv_len)
     return PA_ERR_TABLE;
   if (!aligned16(out) || !aligned16(q_chunk)) return PA_ERR_ALIGN;
+  const pa::PrefillPlan plan = pa::plan_prefill(q_len, start_pos, causal ? 1 : 0, block_size, num_kv_heads);
+  if (plan.bytes) {
+    if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
+  }
   return launch_status(pa::launch_prefill(out, q_chunk, q_len, start_pos, causal, k_cache,
                                           v_cache, page_stride, block_table, block_size, scale,
-                                          num_kv_heads, static_cast<hipStream_t>(stream)));
+                                          num_kv_heads, plan, workspace,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 int pa_decode_input_prep(const int64_t* sampled_token_ids, int64_t position, int32_t* input_ids,
@@ -255,7 +279,7 @@ const char* pa_strerror(int code) {
     case PA_ERR_BLOCK_SIZE: return "block_size must be >= 1";
     case PA_ERR_UNSUPPORTED: return "unsupported shape: need head_dim 256, num_q_heads = 6 * num_kv_heads, 1 <= num_kv_heads <= 64";
     case PA_ERR_SIZE: return "a count or position is out of range";
-    case PA_ERR_WORKSPACE: return "decode workspace is NULL or smaller than pa_decode_workspace_size()";
+    case PA_ERR_WORKSPACE: return "workspace is NULL or smaller than pa_decode_workspace_size() / pa_prefill_workspace_size()";
     case PA_ERR_TABLE: return "the block table has fewer entries than the lengths need";
     case PA_ERR_STRIDE: return "page_stride is smaller than one page";
     case PA_ERR_ALIGN: return "a tensor is not aligned (bf16 tensors: 16 bytes, workspace: 256 bytes)";

@@ -61,10 +61,26 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          const DecodePlan& plan, void* workspace, const DecodeAppend* append,
                          hipStream_t stream);
 
+// Chunked prefill work plan: how many items (query head x 128-row tile) run
+// whole, and how the rest are cut along their key groups.
+constexpr int kPrefillSlots = 256;      // workgroups per round: one per MI355X CU
+constexpr int kPrefillMaxSplit = 16;
+struct PrefillPlan {
+  int64_t num_items;
+  int64_t num_full;      // items 0 .. num_full-1 (heavy first) run whole
+  int64_t split_items;   // the remaining items, each cut into `split` parts
+  int32_t split;
+  size_t part_o_off, part_ml_off, bytes;   // workspace layout (bytes = 0: none needed)
+};
+
+PrefillPlan plan_prefill(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size,
+                         int32_t num_kv_heads);
+
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32_t start_pos,
                           int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
                           int64_t page_stride, const int32_t* block_table, int32_t block_size,
-                          float scale, int32_t num_kv_heads, hipStream_t stream);
+                          float scale, int32_t num_kv_heads, const PrefillPlan& plan,
+                          void* workspace, hipStream_t stream);
 
 // Single-token decode input preparation (pa_decode_input_prep).
 struct InputPrepArgs {

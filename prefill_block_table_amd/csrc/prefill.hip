@@ -32,6 +32,7 @@
 // that cross the diagonal or end a page early.
 #include <math.h>
 
+#include <algorithm>
 #include <type_traits>
 
 #include "pa_device.h"
@@ -86,7 +87,35 @@ struct PrefillArgs {
   float inv_scale_log2;    // its reciprocal
   int32_t num_kv_heads;
   int32_t num_q_tiles;
+  // Work split (see plan_prefill): items 0 .. num_full-1 (heavy first) get
+  // one workgroup each; each later item is cut into `split` contiguous key
+  // ranges whose partial results go to part_o / part_ml.
+  int32_t num_full;
+  int32_t split;
+  float* part_o;           // [slot][128 rows][256], slot = (item - num_full) * split + part
+  float* part_ml;          // [slot][128 rows][2]: row max (log2 units), row sum
 };
+
+// Item (a query head's 128-row tile) of index J, heaviest (latest rows)
+// first.  Consecutive workgroup ids go to the 8 XCDs in turn; when the KV
+// heads divide the XCDs evenly, every XCD serves one KV head (8 / G XCDs per
+// head, taking alternate entries of that head's heavy-first list), so the K/V
+// a workgroup streams are the ones its XCD's L2 already holds for its
+// neighbours.
+__device__ __forceinline__ void map_item(int J, int G, int T, int& g, int& head, int& tile) {
+  if (8 % G == 0 && (kGqa * G * T) % 8 == 0) {
+    const int x = J & 7, slot = J >> 3;
+    g = x % G;
+    const int k = slot * (8 / G) + x / G;        // 0 .. 6T-1 within KV head g
+    tile = T - 1 - k / kGqa;
+    head = g * kGqa + k % kGqa;
+  } else {
+    const int Hq = G * kGqa;
+    tile = T - 1 - J / Hq;
+    head = J % Hq;
+    g = head / kGqa;
+  }
+}
 
 __device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
@@ -167,28 +196,17 @@ __device__ __forceinline__ int lane_here() {
 __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(16))) char smem[kSmemBytes];
 
-  // Workgroup -> (query head, query tile).  Tiles run heaviest (latest
-  // rows) first.  Consecutive workgroup ids go to the 8 XCDs in turn; when
-  // the KV heads divide the XCDs evenly, every XCD serves one KV head (8 / G
-  // XCDs per head, taking alternate entries of that head's heavy-first
-  // list), so the K/V a workgroup streams are the ones its XCD's L2 already
-  // holds for its neighbours.
-  const int G = a.num_kv_heads;
-  const int T = a.num_q_tiles;
+  // Workgroup -> item (query head, query tile) and, for a split item, the
+  // part of its key groups this workgroup takes.
   const int L = blockIdx.x;
-  int g, head, tile;
-  if (8 % G == 0 && (kGqa * G * T) % 8 == 0) {
-    const int x = L & 7, slot = L >> 3;
-    g = x % G;
-    const int k = slot * (8 / G) + x / G;        // 0 .. 6T-1 within KV head g
-    tile = T - 1 - k / kGqa;
-    head = g * kGqa + k % kGqa;
-  } else {
-    const int Hq_ = G * kGqa;
-    tile = T - 1 - L / Hq_;
-    head = L % Hq_;
-    g = head / kGqa;
+  int item = L, part = -1;
+  if (L >= a.num_full) {
+    const int qq = L - a.num_full;
+    item = a.num_full + qq / a.split;
+    part = qq % a.split;
   }
+  int g, head, tile;
+  map_item(item, a.num_kv_heads, a.num_q_tiles, g, head, tile);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index, uniform per wave: LDS destinations and row bases stay scalar
@@ -234,6 +252,9 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int upp = (B + kGroup - 1) / kGroup;
   const int last_page = (kv_end - 1) / B;
   const int units = last_page * upp + (kv_end - last_page * B + kGroup - 1) / kGroup;
+  // this workgroup's key groups [ga, gb) of the tile
+  const int ga = part < 0 ? 0 : (int)((int64_t)units * part / a.split);
+  const int gb = part < 0 ? units : (int)((int64_t)units * (part + 1) / a.split);
 
   // O^T accumulators: row block rb, d-block db (16 d), register r -> d =
   // 16*db + 4*kq + r of query row 16*rb + c16.
@@ -263,7 +284,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
 
   // Issue cursor: logical page ip, group ig inside it; the block-table entry
   // is read (a scalar load) when the first group of a new page is issued.
-  int ip = 0, ig = 0, ip_loaded = -1;
+  int ip = ga / upp, ig = ga % upp, ip_loaded = -1;
   int64_t ip_base = 0;
   // This wave's share of the next group: rows 8w .. 8w+7 of K and of V, four
   // direct-to-LDS loads each (rows 8w + 2j on lanes 0..31, 8w + 2j + 1 on
@@ -329,21 +350,21 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
 
   char* st0 = smem;
   char* st1 = smem + kStageBytes;
-  issue(st0);
+  if (ga < gb) issue(st0);
 
-  int cp = 0, cg = 0;        // compute cursor (page, group)
+  int cp = ga / upp, cg = ga % upp;        // compute cursor (page, group)
   // One barrier per group: entering iteration u every wave waits for its own
   // loads of group u, then the barrier makes all of group u visible and
   // guarantees every wave has finished group u - 1, whose stage the loads of
   // group u + 1 then overwrite.  Waves 0..3 issue their part of those loads
   // right away, waves 4..7 (the other wave of each SIMD) after their scores,
   // so the two waves of a SIMD do not wait for the CU's load path together.
-  for (int u = 0; u < units; ++u) {
-    char* st = (u & 1) ? st1 : st0;
-    char* nst = (u & 1) ? st0 : st1;
+  for (int u = ga; u < gb; ++u) {
+    char* st = ((u - ga) & 1) ? st1 : st0;
+    char* nst = ((u - ga) & 1) ? st0 : st1;
     PA_WAIT_VMCNT(0);
     PA_BARRIER();
-    const bool more = u + 1 < units;
+    const bool more = u + 1 < gb;
     if (more && w < 4) issue(nst);
 
     const int key0 = cp * B + cg * kGroup;
@@ -499,10 +520,11 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     }
   }
 
-  // Merge the two key halves of every row, then normalize and store.  Lane
-  // (kq, c16) holds d = 16*db + 4*kq + r of query row 16*rb + c16; wave w
-  // finishes d-blocks 8*kh .. 8*kh+7 and hands its partner (w ^ 4) the
-  // other eight.  Lane-derived values are recomputed here rather than kept
+  // Merge the two key halves of every row, then normalize and store (or, for
+  // a part of a split item, store the unnormalised partial with its row max
+  // and sum).  Lane (kq, c16) holds d = 16*db + 4*kq + r of query row 16*rb +
+  // c16; wave w finishes d-blocks 8*kh .. 8*kh+7 and hands its partner
+  // (w ^ 1) the other eight.  Lane-derived values are recomputed here rather than kept
   // in registers across the loop.
   const int lane_e = __lane_id();
   float l_tot[2];
@@ -534,9 +556,29 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
       const float M = fmaxf(m_run[rb], mp);
       const float f = fast_exp2(m_run[rb] - M);
       const float fp = fast_exp2(mp - M);
-      const float inv = 1.f / (f * l_tot[rb] + fp * lp);
-      const float fa = f * inv, fb = fp * inv;
+      const float lsum = f * l_tot[rb] + fp * lp;
       const int row = wrow0 + 16 * rb + (lane_e & 15);
+      if (part >= 0) {
+        if (row < a.q_len) {
+          const int64_t slot = (int64_t)(item - a.num_full) * a.split + part;
+          const int trow = row - q0;
+          float* po = a.part_o + (slot * kBM + trow) * kHeadDim + 4 * (lane_e >> 4);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const f32x4 x = o[8 * mine + j][rb];
+            const f32x4 y = xo_peer[(rb * 8 + j) * 64 + lane_e];
+            *reinterpret_cast<f32x4*>(po + 16 * (8 * mine + j)) =
+                f32x4{x[0] * f + y[0] * fp, x[1] * f + y[1] * fp, x[2] * f + y[2] * fp, x[3] * f + y[3] * fp};
+          }
+          if (mine == 0 && (lane_e >> 4) == 0) {
+            a.part_ml[(slot * kBM + trow) * 2] = M;
+            a.part_ml[(slot * kBM + trow) * 2 + 1] = lsum;
+          }
+        }
+        continue;
+      }
+      const float inv = 1.f / lsum;
+      const float fa = f * inv, fb = fp * inv;
       if (row < a.q_len) {
         uint16_t* op = a.out + (int64_t)row * q_stride + head * kHeadDim + 4 * (lane_e >> 4);
 #pragma unroll
@@ -557,12 +599,78 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   else finish(std::integral_constant<int, 1>{});
 }
 
+// Combine the parts of the split items: workgroup (split item, 4-row block),
+// thread (row, 4 dims); parts in order, so results are bitwise repeatable.
+__global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
+  const int item_idx = blockIdx.x / (kBM / 4);
+  const int trow = 4 * (blockIdx.x % (kBM / 4)) + (threadIdx.x >> 6);
+  const int d = 4 * (threadIdx.x & 63);
+  int g, head, tile;
+  map_item(a.num_full + item_idx, a.num_kv_heads, a.num_q_tiles, g, head, tile);
+  const int row = tile * kBM + trow;
+  if (row >= a.q_len) return;
+  float M = kMinusHuge;
+  for (int k = 0; k < a.split; ++k) {
+    const int64_t slot = (int64_t)item_idx * a.split + k;
+    M = fmaxf(M, a.part_ml[(slot * kBM + trow) * 2]);
+  }
+  float lsum = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < a.split; ++k) {
+    const int64_t slot = (int64_t)item_idx * a.split + k;
+    const float f = fast_exp2(a.part_ml[(slot * kBM + trow) * 2] - M);
+    lsum += f * a.part_ml[(slot * kBM + trow) * 2 + 1];
+    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (slot * kBM + trow) * kHeadDim + d);
+    acc += f * v;
+  }
+  const float inv = 1.f / lsum;
+  const int64_t q_stride = (int64_t)a.num_kv_heads * kGqa * kHeadDim;
+  *reinterpret_cast<u32x2*>(a.out + (int64_t)row * q_stride + head * kHeadDim + d) =
+      u32x2{pack_bf16x2(acc[0] * inv, acc[1] * inv), pack_bf16x2(acc[2] * inv, acc[3] * inv)};
+}
+
+int tile_units(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size, int tile) {
+  const int64_t kv_end = causal ? (int64_t)start_pos + std::min<int64_t>((int64_t)(tile + 1) * kBM, q_len)
+                                : (int64_t)start_pos + q_len;
+  const int64_t upp = (block_size + kGroup - 1) / kGroup;
+  const int64_t last_page = (kv_end - 1) / block_size;
+  return (int)(last_page * upp + (kv_end - last_page * block_size + kGroup - 1) / kGroup);
+}
+
 }  // namespace
+
+PrefillPlan plan_prefill(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size,
+                         int32_t num_kv_heads) {
+  // One workgroup per CU (128 KB of LDS each).  Items fill whole rounds of
+  // kPrefillSlots workgroups heaviest first; the r items of an incomplete last
+  // round (or all items, when there are fewer than the slots) are cut into
+  // `split` parts so that round fills the CUs.  The lightest tile bounds the
+  // split so no part is empty.
+  PrefillPlan p{};
+  const int T = (q_len + kBM - 1) / kBM;
+  const int64_t U = (int64_t)num_kv_heads * kGqa * T;
+  int64_t r = U <= kPrefillSlots ? U : U % kPrefillSlots;
+  int64_t S = r > 0 ? kPrefillSlots / r : 1;
+  const int min_units = tile_units(q_len, start_pos, causal, block_size, 0);
+  if (S > kPrefillMaxSplit) S = kPrefillMaxSplit;
+  if (S > min_units) S = min_units;
+  if (S < 2) { S = 1; r = 0; }
+  p.num_items = U;
+  p.num_full = U - r;
+  p.split = (int32_t)S;
+  p.split_items = r;
+  const size_t slots = (size_t)(r * (S > 1 ? S : 0));
+  p.part_o_off = 0;
+  p.part_ml_off = (slots * kBM * kHeadDim * sizeof(float) + 255) & ~(size_t)255;
+  p.bytes = slots ? p.part_ml_off + ((slots * kBM * 2 * sizeof(float) + 255) & ~(size_t)255) : 0;
+  return p;
+}
 
 hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32_t start_pos,
                           int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
                           int64_t page_stride, const int32_t* block_table, int32_t block_size,
-                          float scale, int32_t num_kv_heads, hipStream_t stream) {
+                          float scale, int32_t num_kv_heads, const PrefillPlan& plan,
+                          void* workspace, hipStream_t stream) {
   PrefillArgs a;
   a.out = out;
   a.q = q;
@@ -578,8 +686,17 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   a.inv_scale_log2 = 1.f / a.scale_log2;
   a.num_kv_heads = num_kv_heads;
   a.num_q_tiles = (q_len + kBM - 1) / kBM;
-  hipLaunchKernelGGL(prefill_kernel, dim3(num_kv_heads * kGqa * a.num_q_tiles), dim3(kWavesPf * 64),
-                     0, stream, a);
+  a.num_full = (int32_t)plan.num_full;
+  a.split = plan.split;
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.part_o_off) : nullptr;
+  a.part_ml = plan.bytes ? reinterpret_cast<float*>(ws + plan.part_ml_off) : nullptr;
+  const int64_t grid = plan.num_full + plan.split_items * plan.split;
+  hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kWavesPf * 64), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || plan.split_items == 0) return e;
+  hipLaunchKernelGGL(prefill_merge_kernel, dim3((uint32_t)(plan.split_items * (kBM / 4))), dim3(256), 0,
+                     stream, a);
   return hipGetLastError();
 }
 

@@ -31,7 +31,8 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused",
                           "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
-                          "pa_prefill_chunk", "pa_page_size_for_hybrid", "pa_decode_input_prep",
+                          "pa_prefill_chunk", "pa_prefill_workspace_size",
+                          "pa_page_size_for_hybrid", "pa_decode_input_prep",
                           "pa_strerror", "pa_build_info"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True).stdout
@@ -125,12 +126,13 @@ def test_workspace_size_monotone():
 def _prefill(**kw):
     args = dict(out=FAKE, q=FAKE, q_len=4096, start=4096, causal=1, k=FAKE, v=FAKE,
                 page_stride=832 * 1024, bt=FAKE, n_bt=10, B=832, scale=0.0625, hq=24, hkv=4,
-                d=256)
+                d=256, ws=None, ws_bytes=0)
     args.update(kw)
     return pa.lib.pa_prefill_chunk(args["out"], args["q"], args["q_len"], args["start"],
                                    args["causal"], args["k"], args["v"], args["page_stride"],
                                    args["bt"], args["n_bt"], args["B"], args["scale"],
-                                   args["hq"], args["hkv"], args["d"], None)
+                                   args["hq"], args["hkv"], args["d"], args["ws"], args["ws_bytes"],
+                                   None)
 
 
 def test_prefill_validation():
@@ -144,6 +146,12 @@ def test_prefill_validation():
     assert _prefill(n_bt=9) == C["PA_ERR_TABLE"]               # 9 * 832 < 8192
     assert _prefill(page_stride=100) == C["PA_ERR_STRIDE"]
     assert _prefill(out=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    # q=1685 at 8192 splits its last round: a workspace is needed
+    need = pa.prefill_workspace_size(1685, 8192, 832)
+    assert need > 0 and pa.prefill_workspace_size(4096, 4096, 832) == 0
+    assert _prefill(q_len=1685, start=8192, n_bt=12) == C["PA_ERR_WORKSPACE"]
+    assert _prefill(q_len=1685, start=8192, n_bt=12, ws=FAKE, ws_bytes=need - 1) == C["PA_ERR_WORKSPACE"]
+    assert _prefill(q_len=1685, start=8192, n_bt=12, ws=FAKE_MIS, ws_bytes=need) == C["PA_ERR_ALIGN"]
     assert _prefill(scale=0.0) == C["PA_ERR_SCALE"]
     assert _prefill(scale=-0.0625) == C["PA_ERR_SCALE"]
     assert _prefill(scale=float("nan")) == C["PA_ERR_SCALE"]

@@ -114,3 +114,31 @@ def test_single_kv_head_shard():
     got = run_chunks_gpu(c)
     ref = run_chunks_oracle(c)
     compare(got[0], ref[0], c.name)
+
+
+# Chunks whose items do not fill whole rounds of 256 workgroups: the items of
+# the last round are cut along their key groups and combined by a second
+# launch (q=128 @ 8192: 24 items, 10 parts each; q=1 @ 32767: 24 items of one
+# row; q=300 @ 5000 on page 16: 72 items, 3 parts; q=1685 @ 8192 is covered by
+# the 8K test above).
+SPLIT = [
+    (832, 8192, 128),
+    (784, 32767, 1),
+    (16, 5000, 300),
+    (1024, 2000, 640),
+]
+
+
+@pytest.mark.parametrize("idx", range(len(SPLIT)))
+def test_split_chunks_all_rows(idx):
+    import prefill_block_table_amd as pa
+    B, start, q_len = SPLIT[idx]
+    assert pa.prefill_workspace_size(q_len, start, B) > 0, "expected a split plan"
+    c = W.make_prefill_case(f"split{idx}_b{B}", 90 + idx, [(start, q_len)], B,
+                            -(-(start + q_len) // B) + 3)
+    log(f"{c.name} start={start} q_len={q_len}")
+    got = run_chunks_gpu(c)
+    ref = run_chunks_oracle(c)
+    compare(got[0], ref[0], c.name)
+    again = run_chunks_gpu(c)
+    assert np.array_equal(got[0], again[0]), "split path not repeatable"
