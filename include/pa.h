@@ -224,6 +224,36 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                      int32_t head_dim, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Prefill attention for several sequences in one launch, in the vendor
+ * interface's form ([ALIGN] §6: q, k, v, cu_seqlens_q, seqused_k,
+ * block_table, max_seqlen_q, max_seqlen_k, causal; the page itself calls it
+ * for one sequence).  Sequence s has query rows cu_seqlens_q[s] ..
+ * cu_seqlens_q[s+1]-1 of q and out and seqused_k[s] keys (its own chunk's K/V
+ * included, already in the cache); its rows are the last q_len_s positions:
+ * row i sits at position seqused_k[s] - q_len_s + i, so with causal != 0 it
+ * attends keys 0 .. seqused_k[s] - q_len_s + i and otherwise all
+ * seqused_k[s] keys.  The same kernel as pa_prefill_chunk.
+ *
+ * out, q         bf16 [total_q][num_q_heads][256].
+ * cu_seqlens_q   int32 [num_seqs + 1], non-decreasing, cu_seqlens_q[num_seqs]
+ *                <= total_q.  seqused_k int32 [num_seqs].
+ * block_table    int32 [num_seqs][bt_stride]; bt_stride * block_size >=
+ *                max_seqlen_k.
+ * max_seqlen_q, max_seqlen_k   host bounds of the device lengths (lengths
+ *                above them are clamped to them).  A sequence with no rows,
+ *                or with fewer keys than rows, is left unwritten.
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE,
+ * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
+ */
+int pa_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
+                      const int32_t* cu_seqlens_q, const int32_t* seqused_k, int32_t num_seqs,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal,
+                      const uint16_t* k_cache, const uint16_t* v_cache, int64_t page_stride,
+                      const int32_t* block_table, int32_t bt_stride, int32_t block_size,
+                      float scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      void* stream);
+
+/*
  * Bytes of device workspace pa_prefill_chunk needs for this chunk shape (0
  * when the chunk's items fill whole rounds of workgroups).  bytes_out: host
  * pointer.  Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED,

@@ -25,6 +25,7 @@ from .paged_attention import (  # noqa: F401
     attend,
     decode,
     prefill_chunk,
+    prefill_varlen,
 )
 from .input_prep import decode_input_prep  # noqa: F401
 from .page_geometry import (  # noqa: F401

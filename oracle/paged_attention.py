@@ -207,3 +207,22 @@ def prefill_chunk(q_chunk, start_pos: int, causal: bool, k_cache, v_cache, block
         out[b0:b0 + len(r)] = attend(bf16_bits_to_f64(q_chunk[r]), start_pos + r,
                                      K[:keys], V[:keys], scale, causal=causal)
     return out
+
+
+def prefill_varlen(q, cu_seqlens_q, seqused_k, causal: bool, k_cache, v_cache, block_tables,
+                   block_size: int, scale: float) -> np.ndarray:
+    """Several sequences in one call, the vendor interface's form
+    (page-alignment post §6: cu_seqlens_q, seqused_k, block_table; the page
+    uses it with one sequence): sequence s's rows cu[s]..cu[s+1]-1 are the last
+    q_len_s of its seqused_k[s] tokens, i.e. a chunk at start_pos =
+    seqused_k[s] - q_len_s.  Returns the rows of every sequence in order."""
+    cu = np.asarray(cu_seqlens_q, dtype=np.int64)
+    used = np.asarray(seqused_k, dtype=np.int64)
+    outs = []
+    for s in range(len(used)):
+        c0, c1 = int(cu[s]), int(cu[s + 1])
+        if c1 <= c0:
+            continue
+        outs.append(prefill_chunk(np.asarray(q)[c0:c1], int(used[s]) - (c1 - c0), causal, k_cache,
+                                  v_cache, np.asarray(block_tables)[s], block_size, scale))
+    return np.concatenate(outs) if outs else np.zeros((0,) + np.shape(q)[1:])

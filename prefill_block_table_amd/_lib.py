@@ -28,6 +28,9 @@ lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32,
                                  _f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
                                  _f32, _i32, _i32, _i32, _vp, _sz, _vp]
+lib.pa_prefill_varlen.argtypes = [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _i64,
+                                  _vp, _i32, _i32, _f32, _i32, _i32, _i32, _vp]
+lib.pa_prefill_varlen.restype = ctypes.c_int
 lib.pa_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
            "pa_decode", "pa_decode_append", "pa_prefill_chunk", "pa_prefill_workspace_size"):
@@ -291,6 +294,34 @@ def decode_append(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, 
                                 float(scale), GQA * H, H, HEAD_DIM, _ptr(k_new), _ptr(v_new),
                                 _ptr(slot_out), _ptr(workspace), workspace.numel(), _stream(q)),
            "pa_decode_append")
+    return out
+
+
+def prefill_varlen(q, k_cache, v_cache, block_table, cu_seqlens_q, seqused_k, max_seqlen_q: int,
+                   max_seqlen_k: int, scale: float, causal: bool = True,
+                   out: torch.Tensor = None) -> torch.Tensor:
+    """Several sequences: q [total_q, 6*Hkv, 256]; sequence s owns rows
+    cu_seqlens_q[s]..cu_seqlens_q[s+1]-1 and sees seqused_k[s] keys through
+    block_table[s] (see pa_prefill_varlen in include/pa.h)."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(q, "q", _BF16, k_cache.device)
+    _need(block_table, "block_table", (torch.int32,), k_cache.device)
+    _need(cu_seqlens_q, "cu_seqlens_q", (torch.int32,), k_cache.device)
+    _need(seqused_k, "seqused_k", (torch.int32,), k_cache.device)
+    total_q = q.shape[0]
+    if q.shape != (total_q, GQA * H, HEAD_DIM):
+        raise ValueError("q must be [total_q, 6 * num_kv_heads, 256]")
+    num_seqs = seqused_k.numel()
+    if cu_seqlens_q.numel() != num_seqs + 1 or block_table.dim() != 2 or block_table.shape[0] < num_seqs:
+        raise ValueError("cu_seqlens_q [S+1], seqused_k [S], block_table [>=S, stride]")
+    if out is None:
+        out = torch.empty_like(q)
+    _need(out, "out", _BF16, k_cache.device)
+    _check(lib.pa_prefill_varlen(_ptr(out), _ptr(q), total_q, _ptr(cu_seqlens_q), _ptr(seqused_k),
+                                 num_seqs, int(max_seqlen_q), int(max_seqlen_k), int(bool(causal)),
+                                 _ptr(k_cache), _ptr(v_cache), stride, _ptr(block_table),
+                                 block_table.shape[1], B, float(scale), GQA * H, H, HEAD_DIM,
+                                 _stream(q)), "pa_prefill_varlen")
     return out
 
 

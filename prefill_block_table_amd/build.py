@@ -20,7 +20,7 @@ SOURCES = ["pa_api.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "input_pre
 # Packed fp32 VALU ops are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-             "-Wno-unused-command-line-argument"]
+             "-Wno-unused-command-line-argument", "-Werror=uninitialized"]
 
 
 def _hipcc() -> str:

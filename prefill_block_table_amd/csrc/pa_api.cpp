@@ -219,6 +219,33 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
                                           static_cast<hipStream_t>(stream)));
 }
 
+int pa_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
+                      const int32_t* cu_seqlens_q, const int32_t* seqused_k, int32_t num_seqs,
+                      int32_t max_seqlen_q, int32_t max_seqlen_k, int32_t causal,
+                      const uint16_t* k_cache, const uint16_t* v_cache, int64_t page_stride,
+                      const int32_t* block_table, int32_t bt_stride, int32_t block_size,
+                      float scale, int32_t num_q_heads, int32_t num_kv_heads, int32_t head_dim,
+                      void* stream) {
+  if (!out || !q || !cu_seqlens_q || !seqused_k || !block_table) return PA_ERR_NULL;
+  if (!scale_ok(scale)) return PA_ERR_SCALE;
+  int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
+  if (rc) return rc;
+  rc = check_heads(num_q_heads, num_kv_heads, head_dim);
+  if (rc) return rc;
+  if (num_seqs < 1 || total_q < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
+      (int64_t)max_seqlen_k + block_size > INT32_MAX)
+    return PA_ERR_SIZE;
+  const int64_t grid = (int64_t)num_seqs * num_q_heads * ((max_seqlen_q + 127) / 128);
+  if (grid > INT32_MAX) return PA_ERR_SIZE;
+  if (bt_stride < 1 || (int64_t)bt_stride * block_size < max_seqlen_k) return PA_ERR_TABLE;
+  if (!aligned16(out) || !aligned16(q)) return PA_ERR_ALIGN;
+  return launch_status(pa::launch_prefill_varlen(out, q, total_q, cu_seqlens_q, seqused_k, num_seqs,
+                                                 max_seqlen_q, max_seqlen_k, causal, k_cache,
+                                                 v_cache, page_stride, block_table, bt_stride,
+                                                 block_size, scale, num_kv_heads,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
 int pa_decode_input_prep(const int64_t* sampled_token_ids, int64_t position, int32_t* input_ids,
                          int64_t* positions, int32_t mrope, int64_t positions_stride,
                          int64_t mrope_delta, int32_t* query_start_loc,

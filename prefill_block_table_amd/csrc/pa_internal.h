@@ -106,6 +106,14 @@ struct InputPrepArgs {
 
 hipError_t launch_decode_input_prep(const InputPrepArgs& a, hipStream_t stream);
 
+hipError_t launch_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
+                                 int64_t page_stride, const int32_t* block_table, int32_t bt_stride,
+                                 int32_t block_size, float scale, int32_t num_kv_heads,
+                                 hipStream_t stream);
+
 extern const char* const kDecodeVariant;
 extern const char* const kPrefillVariant;
 

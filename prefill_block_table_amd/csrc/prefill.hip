@@ -94,6 +94,18 @@ struct PrefillArgs {
   int32_t split;
   float* part_o;           // [slot][128 rows][256], slot = (item - num_full) * split + part
   float* part_ml;          // [slot][128 rows][2]: row max (log2 units), row sum
+  // Several sequences (pa_prefill_varlen; NULL cu_seqlens_q: one sequence,
+  // q_len / start_pos / block_table above): sequence s has query rows
+  // cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and seqused_k[s] keys, its block-table
+  // row at block_table + s * bt_stride; num_q_tiles is then the tile count of
+  // the longest sequence, every sequence gets 6 * num_kv_heads * num_q_tiles
+  // workgroups and those past its rows leave at once.
+  const int32_t* cu_seqlens_q;
+  const int32_t* seqused_k;
+  int32_t bt_stride;
+  int32_t total_q;         // rows of q / out
+  int32_t max_q;           // host bounds the device lengths are clamped to
+  int32_t max_k;
 };
 
 // Item (a query head's 128-row tile) of index J, heaviest (latest rows)
@@ -200,13 +212,31 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   // part of its key groups this workgroup takes.
   const int L = blockIdx.x;
   int item = L, part = -1;
-  if (L >= a.num_full) {
+  int32_t q_len = a.q_len, start_pos = a.start_pos;
+  const int32_t* bt = a.block_table;
+  int64_t row0 = 0;                                  // first q / out row of the sequence
+  if (a.cu_seqlens_q) {
+    const int per_seq = a.num_kv_heads * kGqa * a.num_q_tiles;
+    const int sq = L / per_seq;
+    item = L - sq * per_seq;
+    // device lengths are clamped to the host-checked bounds, so no load
+    // leaves q, out or the sequence's block-table row
+    const int c0 = min(load_const_i32(a.cu_seqlens_q + sq), a.total_q);
+    const int c1 = min(load_const_i32(a.cu_seqlens_q + sq + 1), a.total_q);
+    q_len = min(c1 - c0, a.max_q);
+    const int kv = min(load_const_i32(a.seqused_k + sq), a.max_k);
+    start_pos = kv - q_len;                          // the chunk's rows end at the last key
+    if (c0 < 0 || q_len <= 0 || start_pos < 0) return;
+    row0 = c0;
+    bt = a.block_table + (int64_t)sq * a.bt_stride;
+  } else if (L >= a.num_full) {
     const int qq = L - a.num_full;
     item = a.num_full + qq / a.split;
     part = qq % a.split;
   }
   int g, head, tile;
   map_item(item, a.num_kv_heads, a.num_q_tiles, g, head, tile);
+  if (tile * kBM >= q_len) return;                   // past the sequence's rows (several sequences)
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index, uniform per wave: LDS destinations and row bases stay scalar
@@ -218,18 +248,20 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int64_t row_stride = (int64_t)a.num_kv_heads * kHeadDim;
   const int64_t q_stride = (int64_t)Hq * kHeadDim;
   const int B = a.block_size;
+  const uint16_t* qbase = a.q + row0 * q_stride;
+  uint16_t* obase = a.out + row0 * q_stride;
 
   const int q0 = tile * kBM;
   const int wrow0 = q0 + kRowsPerWave * (w >> 1);            // first query row of this wave
-  const int wave_rows = max(0, min(kRowsPerWave, a.q_len - wrow0));
-  const int wave_first_pos = a.start_pos + wrow0;
+  const int wave_rows = max(0, min(kRowsPerWave, q_len - wrow0));
+  const int wave_first_pos = start_pos + wrow0;
   const int wave_last_pos = wave_first_pos + wave_rows - 1;
   int my_row[2];
   bool row_ok[2];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
     my_row[rb] = wrow0 + 16 * rb + c16;
-    row_ok[rb] = my_row[rb] < a.q_len;
+    row_ok[rb] = my_row[rb] < q_len;
   }
 
   // Q^T as the B operand of S^T = K Q^T (16x16x32): lane supplies column
@@ -237,7 +269,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   u32x4 qb[2][8];
 #pragma unroll
   for (int rb = 0; rb < 2; ++rb) {
-    const uint16_t* qp = a.q + (int64_t)(row_ok[rb] ? my_row[rb] : 0) * q_stride + head * kHeadDim + 8 * kq;
+    const uint16_t* qp = qbase + (int64_t)(row_ok[rb] ? my_row[rb] : 0) * q_stride + head * kHeadDim + 8 * kq;
 #pragma unroll
     for (int ds = 0; ds < 8; ++ds) {
       u32x4 v = {0u, 0u, 0u, 0u};
@@ -246,9 +278,9 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     }
   }
 
-  const int kv_len = a.start_pos + a.q_len;
-  const int tile_last = min(q0 + kBM, a.q_len) - 1;
-  const int kv_end = a.causal ? a.start_pos + tile_last + 1 : kv_len;
+  const int kv_len = start_pos + q_len;
+  const int tile_last = min(q0 + kBM, q_len) - 1;
+  const int kv_end = a.causal ? start_pos + tile_last + 1 : kv_len;
   const int upp = (B + kGroup - 1) / kGroup;
   const int last_page = (kv_end - 1) / B;
   const int units = last_page * upp + (kv_end - last_page * B + kGroup - 1) / kGroup;
@@ -293,7 +325,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   auto issue = [&](char* st) {
     if (ip != ip_loaded) {
       ip_loaded = ip;
-      ip_base = (int64_t)load_const_i32(a.block_table + ip) * page_bytes;
+      ip_base = (int64_t)load_const_i32(bt + ip) * page_bytes;
     }
     const int live = min(kGroup, min(B - ig * kGroup, kv_end - (ip * B + ig * kGroup)));
     const uint32_t gofs = (uint32_t)(ig * kGroup) * rs_bytes;
@@ -559,7 +591,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
       const float lsum = f * l_tot[rb] + fp * lp;
       const int row = wrow0 + 16 * rb + (lane_e & 15);
       if (part >= 0) {
-        if (row < a.q_len) {
+        if (row < q_len) {
           const int64_t slot = (int64_t)(item - a.num_full) * a.split + part;
           const int trow = row - q0;
           float* po = a.part_o + (slot * kBM + trow) * kHeadDim + 4 * (lane_e >> 4);
@@ -579,8 +611,8 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
       }
       const float inv = 1.f / lsum;
       const float fa = f * inv, fb = fp * inv;
-      if (row < a.q_len) {
-        uint16_t* op = a.out + (int64_t)row * q_stride + head * kHeadDim + 4 * (lane_e >> 4);
+      if (row < q_len) {
+        uint16_t* op = obase + (int64_t)row * q_stride + head * kHeadDim + 4 * (lane_e >> 4);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const f32x4 x = o[8 * mine + j][rb];
@@ -688,6 +720,12 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   a.num_q_tiles = (q_len + kBM - 1) / kBM;
   a.num_full = (int32_t)plan.num_full;
   a.split = plan.split;
+  a.cu_seqlens_q = nullptr;
+  a.seqused_k = nullptr;
+  a.bt_stride = 0;
+  a.total_q = q_len;
+  a.max_q = q_len;
+  a.max_k = start_pos + q_len;
   char* ws = static_cast<char*>(workspace);
   a.part_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.part_o_off) : nullptr;
   a.part_ml = plan.bytes ? reinterpret_cast<float*>(ws + plan.part_ml_off) : nullptr;
@@ -697,6 +735,43 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   if (e != hipSuccess || plan.split_items == 0) return e;
   hipLaunchKernelGGL(prefill_merge_kernel, dim3((uint32_t)(plan.split_items * (kBM / 4))), dim3(256), 0,
                      stream, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
+                                 const int32_t* cu_seqlens_q, const int32_t* seqused_k,
+                                 int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,
+                                 int32_t causal, const uint16_t* k_cache, const uint16_t* v_cache,
+                                 int64_t page_stride, const int32_t* block_table, int32_t bt_stride,
+                                 int32_t block_size, float scale, int32_t num_kv_heads,
+                                 hipStream_t stream) {
+  PrefillArgs a;
+  a.out = out;
+  a.q = q;
+  a.k_cache = k_cache;
+  a.v_cache = v_cache;
+  a.page_stride = page_stride;
+  a.block_table = block_table;
+  a.q_len = 0;
+  a.start_pos = 0;
+  a.causal = causal ? 1 : 0;
+  a.block_size = block_size;
+  a.scale_log2 = scale * 1.4426950408889634f;
+  a.inv_scale_log2 = 1.f / a.scale_log2;
+  a.num_kv_heads = num_kv_heads;
+  a.num_q_tiles = (max_seqlen_q + kBM - 1) / kBM;
+  a.num_full = INT32_MAX;          // no split
+  a.split = 1;
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.cu_seqlens_q = cu_seqlens_q;
+  a.seqused_k = seqused_k;
+  a.bt_stride = bt_stride;
+  a.total_q = total_q;
+  a.max_q = max_seqlen_q;
+  a.max_k = max_seqlen_k;
+  const int64_t grid = (int64_t)num_seqs * num_kv_heads * kGqa * a.num_q_tiles;
+  hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kWavesPf * 64), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol():
     names = _declared()
     assert set(names) == {"pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused",
                           "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
-                          "pa_prefill_chunk", "pa_prefill_workspace_size",
+                          "pa_prefill_chunk", "pa_prefill_workspace_size", "pa_prefill_varlen",
                           "pa_page_size_for_hybrid", "pa_decode_input_prep",
                           "pa_strerror", "pa_build_info"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
@@ -198,3 +198,23 @@ def test_decode_input_prep_validation():
     assert call(sl_len=0) == C["PA_ERR_SIZE"]
     assert call(G=-1) == C["PA_ERR_SIZE"]
     assert call(mrope=1, stride=0) == C["PA_ERR_SIZE"]
+
+
+def test_prefill_varlen_validation():
+    L = pa.lib
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, total=100, cu=FAKE, su=FAKE, S=3, mq=60, mk=5000, causal=1,
+                 k=FAKE, v=FAKE, ps=832 * 1024, bt=FAKE, bts=7, B=832, scale=0.0625, hq=24, hkv=4, d=256)
+        a.update(kw)
+        return L.pa_prefill_varlen(a["out"], a["q"], a["total"], a["cu"], a["su"], a["S"], a["mq"], a["mk"],
+                                   a["causal"], a["k"], a["v"], a["ps"], a["bt"], a["bts"], a["B"],
+                                   a["scale"], a["hq"], a["hkv"], a["d"], None)
+    assert call(cu=None) == C["PA_ERR_NULL"]
+    assert call(su=None) == C["PA_ERR_NULL"]
+    assert call(S=0) == C["PA_ERR_SIZE"]
+    assert call(mq=0) == C["PA_ERR_SIZE"]
+    assert call(total=0) == C["PA_ERR_SIZE"]
+    assert call(bts=6) == C["PA_ERR_TABLE"]          # 6 * 832 < 5000
+    assert call(scale=-1.0) == C["PA_ERR_SCALE"]
+    assert call(hq=32) == C["PA_ERR_UNSUPPORTED"]
+    assert call(q=FAKE_MIS) == C["PA_ERR_ALIGN"]

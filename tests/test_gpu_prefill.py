@@ -142,3 +142,43 @@ def test_split_chunks_all_rows(idx):
     compare(got[0], ref[0], c.name)
     again = run_chunks_gpu(c)
     assert np.array_equal(got[0], again[0]), "split path not repeatable"
+
+
+# Several sequences in one call (pa_prefill_varlen): mixed lengths, a
+# sequence with no rows, page sizes 832 / 16 / 784, causal and not.
+VARLEN = [
+    (832, [(0, 1), (700, 300), (4000, 129), (2496, 64)]),
+    (16, [(33, 150), (0, 20), (1000, 0), (500, 1)]),
+    (784, [(0, 256), (5000, 2)]),
+]
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("idx", range(len(VARLEN)))
+def test_varlen_all_rows(idx, causal):
+    import torch
+    pa = _pa()
+    B, seqs = VARLEN[idx]
+    pages = sum(-(-(s0 + n) // B) for s0, n in seqs)
+    c = W.make_varlen_prefill_case(f"varlen{idx}_b{B}", 80 + idx, seqs, B, pages + 4, causal=causal)
+    log(f"{c.name} seqs={seqs} causal={causal}")
+    k, v = to_dev(c.k_cache), to_dev(c.v_cache)
+    bt = to_dev(c.block_tables)
+    kh, vh = c.k_cache, c.v_cache
+    for s, ch in enumerate(c.chunks):
+        if ch.q_len == 0:
+            continue
+        pos = np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64)
+        seq = np.full(ch.q_len, s, dtype=np.int32)
+        pa.kv_write_fused(k, v, to_dev(ch.k_new), to_dev(ch.v_new), to_dev(pos), bt, to_dev(seq))
+        kh, vh = oracle.kv_write(kh, vh, ch.k_new, ch.v_new,
+                                 oracle.slot_mapping(pos, None, c.block_tables[s], B))
+    lens = [ch.q_len for ch in c.chunks]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    used = np.array([ch.start_pos + ch.q_len for ch in c.chunks], dtype=np.int32)
+    q = np.concatenate([ch.q for ch in c.chunks])
+    out = pa.prefill_varlen(to_dev(q), k, v, bt, to_dev(cu), to_dev(used), max(lens), int(used.max()),
+                            c.scale, causal=causal)
+    _sync()
+    ref = oracle.prefill_varlen(q, cu, used, causal, kh, vh, c.block_tables, B, c.scale)
+    compare(bits(out), ref, c.name)

@@ -595,3 +595,31 @@ def test_input_prep_mrope_offset_and_is_token_ids():
                                    slot_mappings=slots, mrope=True, mrope_delta=-37, is_token_ids=itk, **bufs)
     assert out["positions"][:, 0].tolist() == [63, 63, 63]
     assert out["is_token_ids"][0] == 1 and not out["is_token_ids"][1:].any()
+
+
+# ---- several sequences in one prefill call -----------------------------------
+
+def test_prefill_varlen_reduces_to_chunks_and_is_order_free():
+    """One sequence reproduces prefill_chunk bitwise; reordering the sequences
+    (rows and tables together) reorders the output rows and nothing else."""
+    import workloads as W
+    c = W.make_varlen_prefill_case("vl_pin", 7, [(5, 3), (0, 4), (17, 2)], 8, 12, hkv=1, hq=6, d=8,
+                                   fill_bits=0)
+    k, v = c.k_cache, c.v_cache
+    for s, ch in enumerate(c.chunks):
+        pos = np.arange(ch.start_pos, ch.start_pos + ch.q_len)
+        k, v = oracle.kv_write(k, v, ch.k_new, ch.v_new, oracle.slot_mapping(pos, None, c.block_tables[s], 8))
+    q = np.concatenate([ch.q for ch in c.chunks])
+    lens = [ch.q_len for ch in c.chunks]
+    cu = np.concatenate([[0], np.cumsum(lens)])
+    used = [ch.start_pos + ch.q_len for ch in c.chunks]
+    got = oracle.prefill_varlen(q, cu, used, True, k, v, c.block_tables, 8, 0.3)
+    for s, ch in enumerate(c.chunks):
+        want = oracle.prefill_chunk(ch.q, ch.start_pos, True, k, v, c.block_tables[s], 8, 0.3)
+        assert np.array_equal(got[cu[s]:cu[s + 1]], want)
+    order = [2, 0, 1]
+    q2 = np.concatenate([c.chunks[i].q for i in order])
+    cu2 = np.concatenate([[0], np.cumsum([lens[i] for i in order])])
+    got2 = oracle.prefill_varlen(q2, cu2, [used[i] for i in order], True, k, v, c.block_tables[order], 8, 0.3)
+    for j, i in enumerate(order):
+        assert np.array_equal(got2[cu2[j]:cu2[j + 1]], got[cu[i]:cu[i + 1]])

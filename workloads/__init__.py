@@ -215,6 +215,42 @@ def decode_8k(seed: int = 2, fill_bits: int = BF16_QNAN) -> DecodeCase:
     return make_decode_case("decode_ctx8192_b832", seed, [8192], 832, 64, fill_bits=fill_bits)
 
 
+@dataclasses.dataclass
+class VarlenPrefillCase:
+    """Several sequences, one chunk each, in one call: sequence s holds tokens
+    [0, start_s) in the cache and prefills q_len_s more (its K/V to write first)."""
+    name: str
+    block_size: int
+    num_pages: int
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    block_tables: np.ndarray  # int32 [S, max_pages]
+    chunks: List[PrefillChunk]
+    causal: bool = True
+    scale: float = SCALE
+
+
+def make_varlen_prefill_case(name: str, seed: int, seqs, block_size: int, num_pages: int,
+                             causal: bool = True, fill_bits: int = BF16_QNAN,
+                             hkv: int = NUM_KV_HEADS, hq: int = NUM_Q_HEADS,
+                             d: int = HEAD_DIM) -> VarlenPrefillCase:
+    """``seqs`` is a list of (start_pos, q_len), one chunk per sequence."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    seqs = [(int(s0), int(n)) for s0, n in seqs]
+    pages = [_pages_for(s0 + n, block_size) for s0, n in seqs]
+    sentinel = num_pages - 1
+    bts = _tables(rng, num_pages, pages, sentinel)
+    k, v = _fill_pool(rng, num_pages, block_size, list(bts), [s0 for s0, _ in seqs], hkv, d, fill_bits)
+    chunks = [PrefillChunk(n, s0, None, None, None) for s0, n in seqs]
+    for c in chunks:
+        c.q = normal_bf16(rng, (c.q_len, hq, d))
+    for c in chunks:
+        c.k_new = normal_bf16(rng, (c.q_len, hkv, d))
+    for c in chunks:
+        c.v_new = normal_bf16(rng, (c.q_len, hkv, d))
+    return VarlenPrefillCase(name, block_size, num_pages, k, v, bts, chunks, causal)
+
+
 def prefill_8k(seed: int = 3, fill_bits: int = BF16_QNAN) -> PrefillCase:
     """Chunk q=4096 at start 4096, then q=1685 at start 8192; page 832, pool 128."""
     return make_prefill_case("prefill_q4096_s4096_then_q1685_b832", seed,
