@@ -13,6 +13,10 @@ causal attention, with no key skipped and the causal range not shortened
 the block table and runs softmax(scale * q K^T) V in float64, one query head
 at a time.
 
+``gemv`` holds the decode-time bf16 M=1 linear layer y = W x, in float64
+and in the library's fixed fp32 summation order (pinned by
+``tests/test_oracle_gemv.py``).
+
 Pinned by ``tests/test_oracle_pins.py`` (brute force, closed forms,
 invariants, a library routine and the pages' printed page facts).
 """
@@ -35,3 +39,4 @@ from .page_geometry import (  # noqa: F401
     required_page_tokens,
     smallest_aligned_page,
 )
+from .gemv import fp32_sum_error_bound, gemv_f64, gemv_fp32  # noqa: F401

@@ -271,3 +271,18 @@ def batched_decode(seed: int = 5, fill_bits: int = BF16_QNAN) -> DecodeCase:
     ctx = rng.integers(4096, 32768, size=16, endpoint=True)
     return make_decode_case("decode_batch16_ctx4k_32k_b832", seed, ctx, 832, 1024,
                             fill_bits=fill_bits)
+
+
+# Decode-time linear layers (long-context inference measurement post,
+# luanjiahao.me 2026-07-17, §5): weight shapes N x K.
+GEMV_SHAPES = ((14336, 5120), (16384, 5120), (34816, 5120))
+
+
+def make_gemv_case(seed: int, N: int, K: int, w_std: float = 0.02):
+    """(W [N, K], x [K]) as bf16 bit patterns: W ~ N(0, w_std^2), the scale of
+    a trained projection's weights, and x ~ N(0, 1), a normalised activation;
+    both drawn in float32 and rounded to bf16.  Draw order: W, then x."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    W = f32_to_bf16_bits(rng.standard_normal(size=(N, K), dtype=np.float32) * np.float32(w_std))
+    x = normal_bf16(rng, (K,))
+    return W, x
