@@ -42,6 +42,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--prefill-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: 5 launches of each prefill chunk")
+    ap.add_argument("--gemv-pass", action="store_true",
+                    help="only the GEMV leg and a calibration copy (for rocprofv3 runs)")
     ap.add_argument("--counter-pass", action="store_true",
                     help="for rocprofv3 --pmc runs: a few headline decode steps, then a "
                          "256 MiB device-to-device copy that calibrates FETCH_SIZE/WRITE_SIZE")
@@ -277,6 +279,52 @@ def bench_input_prep(D, pa, iters=2000, warmup=100):
             "host_us_per_call": host_s / iters * 1e6}
 
 
+def bench_gemv(D, pa, W, iters=40, warmup=10, rotate_bytes=1 << 30):
+    """Decode-time bf16 M=1 linear layer y = W x at the measurement post's
+    three weight shapes (warmup 10, 40 timed launches, as there).  Each timed
+    launch reads a different copy of the weights, cycling over at least 1 GiB
+    of copies, so no launch finds its weights in the 256 MB last-level cache,
+    as in a decode step where every layer has its own weights.  Reports the
+    kernel's average launch time (HIP events around each launch) and its
+    weight bandwidth, and torch.mv (the vendor BLAS) under the same rotation."""
+    torch = D.torch
+    out = {}
+    for N, K in W.GEMV_SHAPES:
+        g = torch.Generator(device=D.dev)
+        g.manual_seed(N)
+        w_bytes = N * K * 2
+        copies = max(2, -(-rotate_bytes // w_bytes))
+        Ws = [(torch.randn(N, K, generator=g, device=D.dev) * 0.02).to(torch.bfloat16)
+              for _ in range(copies)]
+        x = torch.randn(K, generator=g, device=D.dev).to(torch.bfloat16)
+        y = torch.empty(N, dtype=torch.bfloat16, device=D.dev)
+        res = {}
+        for name, fn in (("pa_gemv_bf16", lambda w: pa.gemv(w, x, out=y)),
+                         ("torch_mv", lambda w: torch.mv(w, x))):
+            def step(i, ev=None, fn=fn):
+                if ev is not None:
+                    ev[0].record()
+                fn(Ws[i % copies])
+                if ev is not None:
+                    ev[1].record()
+            for i in range(warmup):
+                step(i)
+            torch.cuda.synchronize()
+            _, ts, _ = timed_loop(torch, iters, step, 0.3 * iters + 5)
+            st = _stats(ts)
+            res[name] = {"kernel_ms_avg": round(st["kernel_ms_avg"], 6),
+                         "kernel_ms_p50": round(st["kernel_ms_p50"], 6),
+                         "weight_gbs": round(w_bytes / (st["kernel_ms_avg"] * 1e-3) / 1e9, 1)}
+        gbs = res["pa_gemv_bf16"]["weight_gbs"]
+        res["hbm_frac"] = round(gbs / HBM_PEAK_GBS, 4)
+        res["weight_copies"] = copies
+        res["algorithmic_bytes_per_launch"] = w_bytes + 2 * K + 2 * N
+        out[f"{N}x{K}"] = res
+        del Ws
+        torch.cuda.empty_cache()
+    return out
+
+
 def decode_src_sha():
     import hashlib
     with open(DECODE_SRC, "rb") as f:
@@ -312,6 +360,19 @@ def counter_pass(D, pa, W):
         pa.decode_append(q, k, v, bt, sl, case.max_seq_len, case.scale, kn, vn, workspace=ws,
                          out=out)
         torch.cuda.synchronize()
+    src = torch.empty(256 << 20, dtype=torch.uint8, device=D.dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+
+
+def gemv_pass(D, pa, W):
+    """Launch sequence profiled for the GEMV summaries: the GEMV leg (three
+    weight shapes, the library kernel and torch.mv), then a plain 256 MiB copy
+    of known size that calibrates the HBM byte counters."""
+    torch = D.torch
+    print(json.dumps({"gemv_bf16_m1": bench_gemv(D, pa, W)}), flush=True)
     src = torch.empty(256 << 20, dtype=torch.uint8, device=D.dev).fill_(1)
     dst = torch.empty_like(src)
     for _ in range(3):
@@ -380,6 +441,9 @@ def main():
     if args.prefill_pass:
         prefill_pass(D, pa, W)
         return
+    if args.gemv_pass:
+        gemv_pass(D, pa, W)
+        return
 
     head_case = W.decode_8k()
     print("[bench] decode_ctx8192_b832 rotated", file=sys.stderr, flush=True)
@@ -403,6 +467,8 @@ def main():
                                                               args.warmup, rotate=True)
         print("[bench] decode input prep", file=sys.stderr, flush=True)
         extra["decode_input_prep"] = bench_input_prep(D, pa)
+        print("[bench] gemv", file=sys.stderr, flush=True)
+        extra["gemv_bf16_m1"] = bench_gemv(D, pa, W)
         print("[bench] prefill", file=sys.stderr, flush=True)
         extra["prefill_b832"] = bench_prefill(D, pa, W.prefill_8k(), max(10, args.steps // 5),
                                               min(args.warmup, 5))

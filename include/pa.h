@@ -9,6 +9,8 @@
  *  [PREP]  jsqmd.com/news/1214744, "2026 先导杯实战：别只盯着大算子，把
  *          Qwen3.5 vLLM 单 Token 输入准备搬上 DCU" (single-token decode
  *          input preparation).
+ *  [MEAS]  luanjiahao.me, 2026-07-17, DCU long-context inference
+ *          measurement (decode-time linear layers, §4-§5).
  *
  * Conventions shared by every call
  *  - Every pointer argument is a DEVICE pointer (memory the caller allocated
@@ -318,6 +320,29 @@ int pa_decode_input_prep(const int64_t* sampled_token_ids, int64_t position, int
  */
 int pa_page_size_for_hybrid(int64_t mamba_page_bytes, int64_t attn_page_bytes_per_token,
                             int32_t alignment_tokens, int32_t* block_size_out);
+
+/*
+ * bf16 M=1 linear layer (GEMV) y = W x for decode ([MEAS] §4: y[j] =
+ * sum_k x[k] * W[j, k], bf16 weights and input, fp32 accumulation; §5: the
+ * 14336 / 16384 / 34816 x 5120 weight shapes).
+ *   y    [N] output: bf16 when y_f32 == 0, float32 when y_f32 != 0
+ *   W    [N, K] bf16, row-major, row stride ldw elements (ldw >= K)
+ *   x    [K] bf16
+ * Summation order, fixed for every launch shape so results are bitwise
+ * repeatable: row j is cut into chunks of 8 consecutive elements; 64 partial
+ * fp32 sums start at +0, sum l takes chunks l, l + 64, l + 128, ... in order
+ * and inside a chunk the elements in order, adding each exact bf16 product
+ * with one rounding (a fused multiply-add); the 64 sums are combined by a
+ * butterfly over index distances 32, 16, 8, 4, 2, 1 (sum_l += sum_(l xor d));
+ * the result is written as fp32 or rounded to bf16 (nearest, ties to even).
+ * W is read once, with streaming (non-temporal) loads; y is written once.
+ * K = 0 gives +0 everywhere; N = 0 launches nothing and checks no pointer.
+ * Errors: PA_ERR_NULL (y, or W / x when N > 0 and K > 0), PA_ERR_SIZE (N < 0,
+ * K < 0, K % 8 != 0, ldw < K, ldw % 8 != 0), PA_ERR_ALIGN (W or x not
+ * 16-byte aligned, y not aligned to its element), PA_ERR_LAUNCH.
+ */
+int pa_gemv_bf16(void* y, int32_t y_f32, const void* W, const void* x, int32_t N, int32_t K,
+                 int64_t ldw, void* stream);
 
 /* Static string naming an error code (never NULL). */
 const char* pa_strerror(int code);

@@ -40,6 +40,8 @@ lib.pa_decode_input_prep.argtypes = [_vp, _i64, _vp, _vp, _i32, _i64, _i64, _vp,
 lib.pa_decode_input_prep.restype = ctypes.c_int
 lib.pa_page_size_for_hybrid.argtypes = [_i64, _i64, _i32, ctypes.POINTER(_i32)]
 lib.pa_page_size_for_hybrid.restype = ctypes.c_int
+lib.pa_gemv_bf16.argtypes = [_vp, _i32, _vp, _vp, _i32, _i32, _i64, _vp]
+lib.pa_gemv_bf16.restype = ctypes.c_int
 lib.pa_strerror.argtypes = [ctypes.c_int]
 lib.pa_strerror.restype = ctypes.c_char_p
 lib.pa_build_info.argtypes = []
@@ -225,6 +227,28 @@ def page_size_for_hybrid(mamba_page_bytes: int, attn_page_bytes_per_token: int =
                                        int(alignment_tokens), ctypes.byref(out)),
            "pa_page_size_for_hybrid")
     return out.value
+
+
+def gemv(W: torch.Tensor, x: torch.Tensor, out: torch.Tensor = None,
+         out_dtype: torch.dtype = torch.bfloat16) -> torch.Tensor:
+    """y = W x for bf16 W [N, K] (row stride ldw = W.stride(0)) and bf16 x [K];
+    y is bf16 or float32 [N] (see pa_gemv_bf16 in include/pa.h)."""
+    _need(W, "W", _BF16, contiguous=False)
+    _need(x, "x", _BF16, device=W.device)
+    if W.dim() != 2 or W.stride(1) != 1:
+        raise ValueError("W must be [N, K] with unit stride along K")
+    N, K = W.shape
+    if x.dim() != 1 or x.shape[0] != K:
+        raise ValueError("x must be [K]")
+    if out is None:
+        out = torch.empty(N, dtype=out_dtype, device=W.device)
+    _need(out, "out", (torch.bfloat16, torch.float32), device=W.device)
+    if out.shape != (N,):
+        raise ValueError("out must be [N]")
+    ldw = W.stride(0) if (N > 1 and K > 0) else K
+    _check(lib.pa_gemv_bf16(_ptr(out), int(out.dtype == torch.float32), _ptr(W), _ptr(x), N, K,
+                            ldw, _stream(W)), "pa_gemv_bf16")
+    return out
 
 
 def decode_workspace(num_seqs: int, max_seq_len: int, block_size: int, num_kv_heads: int = 4,

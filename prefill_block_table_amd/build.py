@@ -15,7 +15,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB_PATH = os.path.join(HERE, "libpa.so")
-SOURCES = ["pa_api.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "input_prep.hip"]
+SOURCES = ["pa_api.cpp", "kv_write.hip", "decode.hip", "prefill.hip", "input_prep.hip", "gemv.hip"]
 
 # Packed fp32 VALU ops are switched off for all device code.
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

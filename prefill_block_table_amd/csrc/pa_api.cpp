@@ -299,6 +299,18 @@ int pa_page_size_for_hybrid(int64_t mamba_page_bytes, int64_t attn_page_bytes_pe
   return PA_OK;
 }
 
+int pa_gemv_bf16(void* y, int32_t y_f32, const void* W, const void* x, int32_t N, int32_t K,
+                 int64_t ldw, void* stream) {
+  if (N < 0 || K < 0 || (K & 7) || ldw < K || (ldw & 7)) return PA_ERR_SIZE;
+  if (N == 0) return PA_OK;
+  if (!y || (K > 0 && (!W || !x))) return PA_ERR_NULL;
+  const uintptr_t ya = reinterpret_cast<uintptr_t>(y);
+  if ((K > 0 && (!aligned16(W) || !aligned16(x))) || (ya & (y_f32 ? 3u : 1u))) return PA_ERR_ALIGN;
+  return launch_status(pa::launch_gemv(y, y_f32 != 0, static_cast<const uint16_t*>(W),
+                                       static_cast<const uint16_t*>(x), N, K, ldw,
+                                       static_cast<hipStream_t>(stream)));
+}
+
 const char* pa_strerror(int code) {
   switch (code) {
     case PA_OK: return "ok";
@@ -319,7 +331,8 @@ const char* pa_strerror(int code) {
 const char* pa_build_info(void) {
   static const std::string info = std::string("libpa rev=") + PA_GIT_REV +
                                  " target=gfx950 " + pa::kDecodeVariant + " " +
-                                 pa::kPrefillVariant + " kv_write-v1(one-wg-per-token)";
+                                 pa::kPrefillVariant + " kv_write-v1(one-wg-per-token) " +
+                                 pa::gemv_variant();
   return info.c_str();
 }
 

@@ -117,4 +117,9 @@ hipError_t launch_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total
 extern const char* const kDecodeVariant;
 extern const char* const kPrefillVariant;
 
+// bf16 M=1 GEMV y = W x (gemv.hip); y is bf16 or fp32.
+hipError_t launch_gemv(void* y, bool y_f32, const uint16_t* W, const uint16_t* x, int32_t N,
+                       int32_t K, int64_t ldw, hipStream_t stream);
+const char* gemv_variant();
+
 }  // namespace pa

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
                           "pa_prefill_chunk", "pa_prefill_workspace_size", "pa_prefill_varlen",
                           "pa_page_size_for_hybrid", "pa_decode_input_prep",
-                          "pa_strerror", "pa_build_info"}
+                          "pa_gemv_bf16", "pa_strerror", "pa_build_info"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True).stdout
     exported = set(re.findall(r" T (pa_\w+)", out))
@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol():
 
 def test_build_info_and_strerror():
     info = pa.build_info()
-    assert "gfx950" in info and "decode-" in info and "prefill-" in info
+    assert "gfx950" in info and "decode-" in info and "prefill-" in info and "gemv-" in info
     for name, code in _codes().items():
         s = pa.strerror(code)
         assert s and s != "unknown error code", name
@@ -218,3 +218,23 @@ def test_prefill_varlen_validation():
     assert call(scale=-1.0) == C["PA_ERR_SCALE"]
     assert call(hq=32) == C["PA_ERR_UNSUPPORTED"]
     assert call(q=FAKE_MIS) == C["PA_ERR_ALIGN"]
+
+
+def test_gemv_validation():
+    def call(**kw):
+        a = dict(y=FAKE, f32=0, W=FAKE, x=FAKE, N=14336, K=5120, ldw=5120)
+        a.update(kw)
+        return pa.lib.pa_gemv_bf16(a["y"], a["f32"], a["W"], a["x"], a["N"], a["K"], a["ldw"], None)
+    assert call(y=None) == C["PA_ERR_NULL"]
+    assert call(W=None) == C["PA_ERR_NULL"]
+    assert call(x=None) == C["PA_ERR_NULL"]
+    assert call(N=-1) == C["PA_ERR_SIZE"]
+    assert call(K=-8) == C["PA_ERR_SIZE"]
+    assert call(K=5124, ldw=5128) == C["PA_ERR_SIZE"]
+    assert call(ldw=5112) == C["PA_ERR_SIZE"]
+    assert call(ldw=5124) == C["PA_ERR_SIZE"]
+    assert call(W=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    assert call(x=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    assert call(y=ctypes.c_void_p(0x10001)) == C["PA_ERR_ALIGN"]
+    assert call(y=FAKE_MIS, f32=1) == C["PA_ERR_ALIGN"]
+    assert call(N=0, y=None, W=None, x=None) == C["PA_OK"]   # nothing to do, nothing launched
