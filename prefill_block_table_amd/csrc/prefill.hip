@@ -6,13 +6,13 @@
 // allows, none added that it forbids ([ALIGN] §5, §9).
 //
 // Work decomposition (ours): a workgroup of 8 wave64s owns a 128-row query
-// tile of one query head.  Waves w and w + 4 (which share a SIMD) own the
-// same 32 query rows; in every 64-token key group wave w takes keys 0..31
-// and wave w + 4 keys 32..63, each with its own online soft-max, and the two
-// halves are merged once at the end.  Each K or V operand read from LDS so
-// feeds two MFMAs (two 16-row blocks), half the LDS traffic per flop of a
-// 16-row wave, and the two waves of a SIMD overlap each other's LDS reads,
-// soft-max and waits with MFMAs.  Keys stream through LDS one 64-token group
+// tile of one query head.  Waves w and w ^ 1 own the same 32 query rows; in
+// every 64-token key group one takes keys 0..31 and the other keys 32..63,
+// each with its own online soft-max, and the two halves are merged once at
+// the end.  Each K or V operand read from LDS so feeds two MFMAs (two 16-row
+// blocks), half the LDS traffic per flop of a 16-row wave.  Waves w and
+// w + 4 share a SIMD; waves 4..7 run each group's PV one iteration late, so
+// on every SIMD one wave's soft-max meets the other wave's MFMAs.  Keys stream through LDS one 64-token group
 // of one page at a time (the page's tail group is masked when the page size
 // is not a multiple of 64).  Per group and wave, for row blocks rb = 0, 1:
 //   S^T[32 keys x 16 rows] = K[32 x 256] Q_rb^T    (16 MFMA 16x16x32)
@@ -23,8 +23,8 @@
 // The transposed orientation makes P^T's MFMA operand a register-local
 // reinterpretation of S^T's accumulator (keys in the order the accumulator
 // holds them; V^T's operand reads use the same order).  K and V rows go from
-// HBM straight into LDS with the direct-to-LDS load, double-buffered (the
-// next group is in flight while this one is computed), 16-byte chunks
+// HBM straight into LDS with the direct-to-LDS load (two K tiles and three V
+// tiles: the next group is in flight while this one is computed), 16-byte chunks
 // XOR-swizzled by row so operand reads are bank-conflict free; V^T operands
 // come out of LDS with the gfx950 transposing read.  Groups entirely above
 // the causal diagonal of the tile are never visited, a wave skips a key half
@@ -41,7 +41,8 @@
 namespace pa {
 
 const char* const kPrefillVariant =
-    "prefill-v8(bm128,8waves,pairs-32rows-keyhalves,adjacent-pairs,lean-softmax,bn64,mfma16x16x32,st-orient,lds-dma-kv,2stage,"
+    "prefill-v10(bm128,8waves,pairs-32rows-keyhalves,adjacent-pairs,lean-softmax,bn64,mfma16x16x32,st-orient,lds-dma-kv,2k3v-tiles,"
+    "late-pv-on-waves4-7,"
     "tr16-vt,lazy-rescale,heavy-first,xcd-kvhead-map,hw-bf16-pack)";
 
 namespace {
@@ -52,8 +53,7 @@ constexpr int kBM = (kWavesPf / 2) * kRowsPerWave;  // 128 query rows per workgr
 constexpr int kHalfKeys = kGroup / 2;               // keys per wave per group
 constexpr int kRowBytes = kHeadDim * 2;             // one KV head's row: 512 B
 constexpr int kTileBytes = kGroup * kRowBytes;      // 64 rows: 32 KB
-constexpr int kStageBytes = 2 * kTileBytes;         // K tile then V tile
-constexpr int kLoopBytes = 2 * kStageBytes;         // two stages: 128 KB
+constexpr int kLoopBytes = 5 * kTileBytes;          // two K tiles, three V tiles: 160 KB
 // End merge: every wave hands its partner the half of O^T the partner
 // finishes (2 row blocks x 8 d-blocks x 64 lanes x 16 B) plus (m, l).
 constexpr int kXoWaveBytes = 2 * 8 * 64 * 16;
@@ -318,11 +318,11 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   // is read (a scalar load) when the first group of a new page is issued.
   int ip = ga / upp, ig = ga % upp, ip_loaded = -1;
   int64_t ip_base = 0;
-  // This wave's share of the next group: rows 8w .. 8w+7 of K and of V, four
-  // direct-to-LDS loads each (rows 8w + 2j on lanes 0..31, 8w + 2j + 1 on
-  // lanes 32..63).  Rows past the group's live end reload the page's first
+  // This wave's share of the next group: rows 8w .. 8w+7 of K (into K tile
+  // kst) and of V (into V tile vst), four direct-to-LDS loads each (rows
+  // 8w + 2j on lanes 0..31, 8w + 2j + 1 on lanes 32..63).  Rows past the group's live end reload the page's first
   // row (finite; masked out of the softmax).
-  auto issue = [&](char* st) {
+  auto issue = [&](char* kst, char* vst) {
     if (ip != ip_loaded) {
       ip_loaded = ip;
       ip_base = (int64_t)load_const_i32(bt + ip) * page_bytes;
@@ -339,30 +339,29 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const uint32_t rowofs = gofs + (uint32_t)(8 * w + 2 * j) * rs_bytes;
-        char* dst = st + (8 * w + 2 * j) * kRowBytes;
-        __builtin_amdgcn_global_load_lds(kp + rowofs + (k_src ^ (32u * j)), (PA_LDS void*)dst, 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + rowofs + (v_src ^ (64u * j)), (PA_LDS void*)(dst + kTileBytes),
-                                         16, 0, 0);
+        const int ro = (8 * w + 2 * j) * kRowBytes;
+        __builtin_amdgcn_global_load_lds(kp + rowofs + (k_src ^ (32u * j)), (PA_LDS void*)(kst + ro), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + rowofs + (v_src ^ (64u * j)), (PA_LDS void*)(vst + ro), 16, 0, 0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 8 * w + 2 * j + half;
         const uint32_t rb = row < live ? gofs + (uint32_t)row * rs_bytes : 0u;
-        char* dst = st + (8 * w + 2 * j) * kRowBytes;
+        const int ro = (8 * w + 2 * j) * kRowBytes;
         __builtin_amdgcn_global_load_lds(kp + (rb + ((uint32_t)(pos ^ kswz(row)) << 4)),
-                                         (PA_LDS void*)dst, 16, 0, 0);
+                                         (PA_LDS void*)(kst + ro), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vp + (rb + ((uint32_t)(pos ^ vswz(row)) << 4)),
-                                         (PA_LDS void*)(dst + kTileBytes), 16, 0, 0);
+                                         (PA_LDS void*)(vst + ro), 16, 0, 0);
       }
     }
     if (++ig == upp) { ig = 0; ++ip; }
   };
 
-  // Per-lane operand read offsets within a stage (this wave's key half is
-  // rows 32*kh .. 32*kh+31 of the tile).
-  // Stage bases are multiples of 64 KB, so the swizzled bits of an operand
-  // address are XORed onto one per-lane base.
+  // Per-lane operand read offsets within a K or V tile (this wave's key half
+  // is rows 32*kh .. 32*kh+31 of the tile).  Tile bases are multiples of
+  // 32 KB, so the swizzled bits of an operand address are XORed onto one
+  // per-lane base.
   // K A-operand (16x16x32) of key block kb and d-step ds: row 32*kh + 16*kb
   // + c16, 16-byte chunk 4*ds + kq, stored at (4*ds + kq) ^ c16
   // = 16*(ds >> 2) + 4*((ds & 3) ^ (c16 >> 2)) + (kq ^ (c16 & 3)):
@@ -377,37 +376,88 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   // + ((j & 3) >> 1): address v_lane ^ ((db & 7) << 5), immediate
   // 256*(db >> 3) (+ 16 rows).
   const int vm = 4 * (kq & 1) + (c16 >> 2);
-  const uint32_t v_lane = kTileBytes + (uint32_t)(kHalfKeys * kh + 4 * kq + (c16 >> 2)) * kRowBytes +
+  const uint32_t v_lane = (uint32_t)(kHalfKeys * kh + 4 * kq + (c16 >> 2)) * kRowBytes +
                           (vm << 5) + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
 
-  char* st0 = smem;
-  char* st1 = smem + kStageBytes;
-  if (ga < gb) issue(st0);
+  // LDS: K tiles at 0 and 32 KB (group u: tile (u - ga) % 2), V tiles at 64,
+  // 96 and 128 KB (group u: tile (u - ga) % 3).  V has a third tile because
+  // waves 4..7 run the PV of a group one iteration later (see below).
+  auto ktile = [&](int r) { return smem + (r & 1) * kTileBytes; };
+  auto vtile = [&](int r) { return smem + (2 + r % 3) * kTileBytes; };
+  if (ga < gb) issue(ktile(0), vtile(0));
+
+  // P and V tile of the group whose PV comes next.
+  bool pv_go = false;
+  u32x4 pcur[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
+  uint32_t pv_vbase = 0;
 
   int cp = ga / upp, cg = ga % upp;        // compute cursor (page, group)
-  // One barrier per group: entering iteration u every wave waits for its own
-  // loads of group u, then the barrier makes all of group u visible and
-  // guarantees every wave has finished group u - 1, whose stage the loads of
-  // group u + 1 then overwrite.  Waves 0..3 issue their part of those loads
-  // right away, waves 4..7 (the other wave of each SIMD) after their scores,
-  // so the two waves of a SIMD do not wait for the CU's load path together.
+  // One barrier per group.  Waves w and w + 4 share a SIMD.  Waves 0..3 run
+  // each group as scores, softmax, PV; waves 4..7 run the PV of a group at
+  // the start of the next iteration, before that one's scores, so on every
+  // SIMD one wave's softmax (VALU) meets the other wave's MFMAs instead of
+  // both waves idling the matrix unit in the softmax together.  Entering
+  // iteration u every wave waits for its own loads of group u; the barrier
+  // makes all of group u visible and guarantees every wave has finished
+  // iteration u - 1, after which K tile (u + 1) % 2 (group u - 1) and V tile
+  // (u + 1) % 3 (group u - 2; waves 4..7 read it in iteration u - 1) are
+  // free for group u + 1's loads.  Waves 0..3 issue their part right away,
+  // waves 4..7 after their deferred PV.
   for (int u = ga; u < gb; ++u) {
-    char* st = ((u - ga) & 1) ? st1 : st0;
-    char* nst = ((u - ga) & 1) ? st0 : st1;
+    const int r = u - ga;
+    char* const kt = ktile(r);
+    char* const vt = vtile(r);
     PA_WAIT_VMCNT(0);
     PA_BARRIER();
     const bool more = u + 1 < gb;
-    if (more && w < 4) issue(nst);
+    auto pv = [&](const u32x4 (&pbv)[2], const uint32_t vbase) {
+      u32x2 va[2][2][2];
+      // batch b: d-blocks 2*b, 2*b + 1
+      auto vread = [&](int b, u32x2 (&d)[2][2]) {
+        switch (b) {
+#define PA_VR(BB)                                                                        \
+  case BB: {                                                                             \
+    constexpr int db0 = 2 * (BB), db1 = 2 * (BB) + 1;                                    \
+    const uint32_t a0 = vbase ^ ((db0 & 7) << 5), a1 = vbase ^ ((db1 & 7) << 5);         \
+    PA_DS_READ_TR16(d[0][0], a0, 256 * (db0 >> 3));                                      \
+    PA_DS_READ_TR16(d[0][1], a0, 256 * (db0 >> 3) + 16 * kRowBytes);                     \
+    PA_DS_READ_TR16(d[1][0], a1, 256 * (db1 >> 3));                                      \
+    PA_DS_READ_TR16(d[1][1], a1, 256 * (db1 >> 3) + 16 * kRowBytes);                     \
+  } break;
+          PA_VR(0) PA_VR(1) PA_VR(2) PA_VR(3) PA_VR(4) PA_VR(5) PA_VR(6) PA_VR(7)
+#undef PA_VR
+        }
+      };
+      vread(0, va[0]);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const int cur = b & 1;
+        if (b < 7) {
+          vread(b + 1, va[cur ^ 1]);
+          asm volatile("s_waitcnt lgkmcnt(4)"
+                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
+        } else {
+          asm volatile("s_waitcnt lgkmcnt(0)"
+                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
+        }
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
+#pragma unroll
+          for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pbv[rb], o[2 * b + t][rb]);
+        }
+      }
+    };
 
-    const int key0 = cp * B + cg * kGroup;
-    const int n = min(kGroup, min(B - cg * kGroup, kv_end - key0));
-    if (++cg == upp) { cg = 0; ++cp; }
-    const uint32_t sbase = lds_addr(st);
-    const int hk0 = key0 + kHalfKeys * kh;   // first key of this wave's half
-    // The half holds no live key, or (causal) every key of it lies after
-    // the wave's last row: nothing to add.
-    const bool active = wave_rows > 0 && kHalfKeys * kh < n && !(a.causal && hk0 > wave_last_pos);
-
+    auto qksm = [&]() {
+      const int key0 = cp * B + cg * kGroup;
+      const int n = min(kGroup, min(B - cg * kGroup, kv_end - key0));
+      if (++cg == upp) { cg = 0; ++cp; }
+      const int hk0 = key0 + kHalfKeys * kh;   // first key of this wave's half
+      // The half holds no live key, or (causal) every key of it lies after
+      // the wave's last row: nothing to add.
+      const bool active = wave_rows > 0 && kHalfKeys * kh < n && !(a.causal && hk0 > wave_last_pos);
+      if (!active) return false;
     // S^T = K Q^T: key block kb (16 keys), row block rb in s[kb][rb].  LDS
     // reads run one d-step ahead of the MFMAs; each read feeds two MFMAs.
     f32x4 s[2][2];
@@ -415,8 +465,8 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      const uint32_t kbase = sbase + k_lane;
+    {
+      const uint32_t kbase = lds_addr(kt) + k_lane;
       u32x4 kv[2][2];
       // d-step ds: address kbase ^ ((ds & 3) << 6), immediate kb * 8192 + (ds >> 2) * 256
       auto kread = [&](int ds, u32x4 (&d)[2]) {
@@ -447,9 +497,6 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
           for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16(kv[cur][kb], qb[rb][ds], s[kb][rb]);
       }
     }
-    if (more && w >= 4) issue(nst);
-    if (!active) continue;
-
     // Soft-max.  s[kb][rb][r] is key hk0 + 16*kb + 4*kq + r of query row
     // 16*rb + c16; scores stay unscaled until the exponent (one fma).
     const bool need_mask = (kHalfKeys * kh + kHalfKeys > n) || (a.causal && hk0 + kHalfKeys - 1 > wave_first_pos);
@@ -491,7 +538,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         m_run[rb] = m_new;
       }
     }
-    u32x4 pb[2];
+    u32x4 (&pb)[2] = pcur;
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
       // P^T operand: k = 0..3 <- key block 0, k = 4..7 <- key block 1
@@ -509,10 +556,22 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
       for (int j = 0; j < 4; ++j) l_run[rb] = dot2_ones(pb[rb][j], l_run[rb]);
     }
 
-    // O^T += V^T P^T: d-block db, both row blocks.  The reads of a batch
-    // (two d-blocks) run one batch ahead of its MFMAs.
-    {
-      const uint32_t vbase = sbase + v_lane;
+      return true;
+    };
+    if (w < 4) {
+      if (more) issue(ktile(r + 1), vtile(r + 1));
+      pv_go = qksm();
+      pv_vbase = lds_addr(vt) + v_lane;
+    }
+    if (pv_go) pv(pcur, pv_vbase);
+    if (w >= 4) {
+      if (more) issue(ktile(r + 1), vtile(r + 1));
+      pv_go = qksm();
+      pv_vbase = lds_addr(vt) + v_lane;
+    }
+  }
+  if (w >= 4 && pv_go) {
+    auto pv = [&](const u32x4 (&pbv)[2], const uint32_t vbase) {
       u32x2 va[2][2][2];
       // batch b: d-blocks 2*b, 2*b + 1
       auto vread = [&](int b, u32x2 (&d)[2][2]) {
@@ -546,10 +605,12 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         for (int t = 0; t < 2; ++t) {
           const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
 #pragma unroll
-          for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pb[rb], o[2 * b + t][rb]);
+          for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pbv[rb], o[2 * b + t][rb]);
         }
       }
-    }
+    };
+
+    pv(pcur, pv_vbase);
   }
 
   // Merge the two key halves of every row, then normalize and store (or, for
