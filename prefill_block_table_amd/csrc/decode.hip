@@ -15,9 +15,13 @@
 //    flattened step list is cut into one near-equal contiguous range per
 //    workgroup, about one workgroup per CU, so short and long sequences of a
 //    batch are balanced.  Per wave and step:
-//    - K and V rows go from HBM into wave-private LDS with the direct-to-LDS
-//      load (no VGPRs; 16-byte chunks XOR-swizzled by row so the operand reads
-//      below are bank-conflict free), two steps in flight;
+//    - K and V rows go from HBM into registers with plain 16-byte loads,
+//      three steps in flight per wave: each lane's K loads are exactly its
+//      MFMA A operand (row = key, 8 consecutive dims), so K never touches
+//      LDS; V rows pass through a wave-private LDS tile (16-byte chunks
+//      XOR-swizzled by row, so the transposing reads below are bank-conflict
+//      free).  Every load in flight is a register load, so the compiler's
+//      waits on them are exact;
 //    - the 6 query heads of the KV head share every K/V byte read (GQA 6):
 //      S^T[16 keys x 16] = K Q^T is eight 16x16x32 bf16 MFMAs; in this
 //      orientation each lane holds one query head, so the online-softmax max
@@ -48,17 +52,19 @@
 namespace pa {
 
 const char* const kDecodeVariant =
-    "decode-v7(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-lds-dma,2stage,"
-    "mfma16x16x32-qk,tr16-vt,mfma16x16x16-pv,lazy-rescale,append)";
+    "decode-v8(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-in-registers,3-steps-in-flight,"
+    "mfma16x16x32-qk,v-lds-transpose,tr16-vt,mfma16x16x16-pv,lazy-rescale,append)";
 
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kStages = 2;
+constexpr int kStages = 3;                         // steps in flight per wave
 constexpr int kRowBytes = kHeadDim * 2;            // one KV head's row: 512 B
-constexpr int kTileBytes = 16 * kRowBytes;         // 16 K (or V) rows of one wave step: 8 KB
-constexpr int kStageBytes = 2 * kTileBytes;        // K tile then V tile
-constexpr int kSmemBytes = kWaves * kStages * kStageBytes;   // 128 KB
+constexpr int kTileBytes = 16 * kRowBytes;         // 16 V rows of one wave step: 8 KB
+// LDS: one V tile per wave (the transpose buffer); the in-workgroup merge
+// of waves sharing a KV head reuses it.
+constexpr int kMergeLds = kWaves * kGqa * (kHeadDim + 2) * 4;
+constexpr int kSmemBytes = kWaves * kTileBytes > kMergeLds ? kWaves * kTileBytes : kMergeLds;
 constexpr float kRescaleSlack = 8.f;               // log2 headroom before re-basing O
 constexpr int kMergeSlices = 32;                   // partials merged in parallel per dim
 constexpr int kMergeDims = 32;                     // dims per merge workgroup (one 128 B line)
@@ -68,11 +74,6 @@ static_assert(kDecodeWorkgroups <= kMergeSlices * kMergeParts, "one merge round 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 #define PA_LDS __attribute__((address_space(3)))
 
-// Waits on this wave's outstanding memory operations.  Inline asm with a
-// memory clobber, so the compiler cannot move LDS reads of direct-to-LDS
-// data above the wait.  Vector memory operations retire in issue order.
-#define PA_WAIT_VMCNT(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
-#define PA_WAIT_LGKMCNT0() asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory")
 
 struct DecodeArgs {
   uint16_t* out;
@@ -148,11 +149,8 @@ __device__ __forceinline__ float pair32_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
-// K rows: 16-byte chunk c of row r sits at position c ^ (r & 7), so the 8
-// rows of an MFMA-operand read hit 8 different bank quads.  V rows: chunk c
-// at c ^ ((r & 3) << 1), so the 4 rows of a transposing read hit 4 different
-// 32-byte bank groups.
-__device__ __forceinline__ int kswz(int r) { return r & 7; }
+// V rows in the LDS tile: chunk c at c ^ ((r & 3) << 1), so the 4 rows of a
+// transposing read hit 4 different 32-byte bank groups.
 __device__ __forceinline__ int vswz(int r) { return (r & 3) << 1; }
 
 // Read-only metadata (block tables) read at a wave-uniform address: through
@@ -304,27 +302,21 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
   // c ^ ((r & 3) << 1) (bank-conflict-free operand reads, see compute).
   const int pos = lane & 31;
   const int half = lane >> 5;
-  uint32_t koff[8], voff[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int row = 2 * j + half;
-    koff[j] = (uint32_t)row * rs_bytes + ((uint32_t)(pos ^ kswz(row)) << 4);
-    voff[j] = (uint32_t)row * rs_bytes + ((uint32_t)(pos ^ vswz(row)) << 4);
-  }
-  char* stA = smem + w * (kStages * kStageBytes);
-  char* stB = stA + kStageBytes;
-  // Operand read addresses in stage A (stage B: + kStageBytes).
-  // K A-operand: row c16 (key), 16-byte chunk 4*t + kq at position
-  // (4*t + kq) ^ (c16 & 7) = 8*(t >> 1) + (4*((t & 1) ^ (c16 >> 2 & 1)) + (kq ^ (c16 & 3))).
-  const uint32_t kr = lds_addr(stA) + c16 * kRowBytes;
-  const uint32_t k_even = kr + ((((c16 >> 2) & 1) * 4 + (kq ^ (c16 & 3))) << 4);
-  const uint32_t k_odd = kr + (((((c16 >> 2) & 1) ^ 1) * 4 + (kq ^ (c16 & 3))) << 4);
+  // V rows 2*jj + half, chunk pos: source offset within the step (plus
+  // 2*jj rows), and LDS position of the chunk (row-swizzled, see vswz).
+  const uint32_t v_lane_src = (uint32_t)half * rs_bytes + 16u * pos;
+  // This wave's V tile (LDS transpose buffer).
+  char* vt0 = smem + w * kTileBytes;
+  // K A-operand of operand step t: row c16 (key) of the step, 16-byte chunk
+  // 4*t + kq (d = 32*t + 8*kq .. +7): loaded from HBM straight into the
+  // registers that feed the MFMA.
+  const uint32_t k_lane = (uint32_t)c16 * rs_bytes + 16u * kq;
   // V^T operands.  Transposing read: lane (kq, c16) points at
   // V[4*kq + c16/4][16*db + 4*(c16%4)] and receives V[4*kq + e][16*db + c16],
   // e = 0..3: the A operand of V^T.  With the row swizzle the byte offset
   // is 32*((db & 3) ^ (vrow & 3)) + 128*(db >> 2) + 16*h1 + 8*h0.
   const int vrow = 4 * kq + (c16 >> 2);
-  const uint32_t vr = lds_addr(stA) + kTileBytes + vrow * kRowBytes + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
+  const uint32_t vr = lds_addr(vt0) + vrow * kRowBytes + (((c16 & 3) >> 1) << 4) + (c16 & 1) * 8;
   const uint32_t v0 = vr + ((0 ^ (vrow & 3)) << 5);
   const uint32_t v1 = vr + ((1 ^ (vrow & 3)) << 5);
   const uint32_t v2 = vr + ((2 ^ (vrow & 3)) << 5);
@@ -383,7 +375,16 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
     int isp = la - page0 * spp;
     int ip_loaded = -1;
     int64_t ip_base = 0;
-    auto issue = [&](char* st) {
+    // K and V of the steps in flight: kreg[slot][t] / vreg[slot][jj], slot =
+    // step % kStages (relative to la).  All of them are plain loads into
+    // registers, so the compiler's own waits on them are exact.
+    u32x4 kreg[kStages][8];
+    u32x4 vreg[kStages][8];
+    // Step issue into slot j: the 16 K rows of this wave go to kreg[j] (lane
+    // (kq, c16) takes 16 bytes of row c16 per operand step: the MFMA A
+    // operand as it is); the 16 V rows to vreg[j] (lane (half, pos) takes
+    // 16-byte chunk pos of rows 2*jj + half).
+    auto issue = [&](const int j) __attribute__((always_inline)) {
       if (ip != ip_loaded) {
         ip_loaded = ip;
         ip_base = (int64_t)load_const_i32(bt + ip) * page_bytes;
@@ -394,40 +395,41 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
       // masked rows (or, when appending, the new token's row and after)
       const int lim = (append && ip == last_page) ? page_len - 1 : page_len;
       if (kb + 16 <= lim) {
-        const char* kp = kcache + ip_base + (uint32_t)kb * rs_bytes;
-        const char* vp = vcache + ip_base + (uint32_t)kb * rs_bytes;
+        const char* kp = kcache + ip_base + (uint32_t)kb * rs_bytes + k_lane;
+        const char* vp = vcache + ip_base + (uint32_t)kb * rs_bytes + v_lane_src;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          __builtin_amdgcn_global_load_lds(kp + koff[j], (PA_LDS void*)(st + j * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(vp + voff[j], (PA_LDS void*)(st + kTileBytes + j * 1024), 16, 0, 0);
-        }
+        for (int t = 0; t < 8; ++t) kreg[j][t] = *reinterpret_cast<const u32x4*>(kp + 64 * t);
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) vreg[j][jj] = *reinterpret_cast<const u32x4*>(vp + 2 * jj * rs_bytes);
       } else {
         // Tail step: rows at or past lim reload the page's first row
         // (finite; masked out of the softmax) or, when appending, take
         // k_new / v_new.
-        const char* kp = kcache + ip_base;
-        const char* vp = vcache + ip_base;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int row = 2 * j + half;
-          const int key = kb + row;
+        {
+          const int key = kb + c16;
           const bool fresh = key >= lim && append && ip == last_page;
-          const uint32_t roff = (uint32_t)(key < lim ? key : 0) * rs_bytes;
-          const uint32_t kc = (uint32_t)(pos ^ kswz(row)) << 4;
-          const uint32_t vc = (uint32_t)(pos ^ vswz(row)) << 4;
-          __builtin_amdgcn_global_load_lds(fresh ? knew + kc : kp + (roff + kc),
-                                           (PA_LDS void*)(st + j * 1024), 16, 0, 0);
-          __builtin_amdgcn_global_load_lds(fresh ? vnew + vc : vp + (roff + vc),
-                                           (PA_LDS void*)(st + kTileBytes + j * 1024), 16, 0, 0);
+          const char* kp = fresh ? knew + 16 * kq
+                                 : kcache + ip_base + (uint32_t)(key < lim ? key : 0) * rs_bytes + 16 * kq;
+#pragma unroll
+          for (int t = 0; t < 8; ++t) kreg[j][t] = *reinterpret_cast<const u32x4*>(kp + 64 * t);
+        }
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int key = kb + 2 * jj + half;
+          const bool fresh = key >= lim && append && ip == last_page;
+          const char* vp = fresh ? vnew + 16 * pos
+                                 : vcache + ip_base + (uint32_t)(key < lim ? key : 0) * rs_bytes + 16 * pos;
+          vreg[j][jj] = *reinterpret_cast<const u32x4*>(vp);
         }
       }
       if (++isp == spp) { isp = 0; ++ip; }
     };
-    // The first two steps go out before the rest of the setup.  Vector
-    // memory operations retire in issue order: the q (and k_new) loads above
-    // are older than step la's.
-    issue(stA);
-    if (la + 1 < lb) issue(stB);
+    const int nsteps = lb - la;
+    // With at least 2 * kStages steps the first kStages go out
+    // unconditionally on the path that leads to the steady loop, so the
+    // compiler's count of memory operations issued after each K load is
+    // the same on entry and around the loop (no full drain per round).
+    const bool deep = nsteps >= 2 * kStages;
 
     // Softmax state of query head c16.  O^T and l are kept relative to the
     // reference m_run, which is re-based only when a score exceeds it by more
@@ -440,27 +442,28 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
     // Compute cursor (same walk as the issue cursor, one or two steps behind).
     int cp = page0;
     int csp = la - page0 * spp;
-    auto compute = [&](const uint32_t soff) {
+    auto compute = [&](const int j) __attribute__((always_inline)) {
       const int kb = csp * STOK + 16 * ks;
+      // V rows into this wave's LDS tile, chunk c of row r at c ^ vswz(r).
+      // The previous step's reads of the tile have completed (lgkmcnt(0)
+      // below), and one wave's LDS operations run in order.
+      {
+        const int ln = __lane_id(), ps = ln & 31, hf = ln >> 5;
+#pragma unroll
+        for (int jj = 0; jj < 8; ++jj) {
+          const int row = 2 * jj + hf;
+          *reinterpret_cast<u32x4*>(vt0 + row * kRowBytes + ((ps ^ vswz(row)) << 4)) = vreg[j][jj];
+        }
+        // the writes land before the transposing reads below (which the
+        // compiler does not see as memory accesses)
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
       const int page_len = min(B, L - cp * B);
       if (++csp == spp) { csp = 0; ++cp; }
-      // Operand reads from LDS, written as inline asm: the compiler's wait
-      // insertion cannot tell which direct-to-LDS load wrote which bytes and
-      // would otherwise drain every in-flight load (the prefetched step too)
-      // before each read.  The explicit vmcnt wait before compute() orders
-      // these reads after this step's loads; one lgkmcnt wait below, which
-      // takes every result as an operand, orders their uses after the reads.
-      const uint32_t ke = k_even + soff, ko = k_odd + soff;
-      const uint32_t w0 = v0 + soff, w1 = v1 + soff, w2 = v2 + soff, w3 = v3 + soff;
-      u32x4 kv[8];
-      PA_DS_READ_B128(kv[0], ke, 0);
-      PA_DS_READ_B128(kv[1], ko, 0);
-      PA_DS_READ_B128(kv[2], ke, 128);
-      PA_DS_READ_B128(kv[3], ko, 128);
-      PA_DS_READ_B128(kv[4], ke, 256);
-      PA_DS_READ_B128(kv[5], ko, 256);
-      PA_DS_READ_B128(kv[6], ke, 384);
-      PA_DS_READ_B128(kv[7], ko, 384);
+      // V^T operand reads (transposing) as inline asm; one lgkmcnt wait
+      // below, which takes every result as an operand, orders their uses
+      // after the reads.
+      const uint32_t w0 = v0, w1 = v1, w2 = v2, w3 = v3;
       u32x2 va[16];
       PA_DS_READ_TR16(va[0], w0, 0);    PA_DS_READ_TR16(va[1], w1, 0);
       PA_DS_READ_TR16(va[2], w2, 0);    PA_DS_READ_TR16(va[3], w3, 0);
@@ -470,12 +473,14 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
       PA_DS_READ_TR16(va[10], w2, 256); PA_DS_READ_TR16(va[11], w3, 256);
       PA_DS_READ_TR16(va[12], w0, 384); PA_DS_READ_TR16(va[13], w1, 384);
       PA_DS_READ_TR16(va[14], w2, 384); PA_DS_READ_TR16(va[15], w3, 384);
+      // (memory clobber: the next step's writes to the tile stay after the reads)
       asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(kv[0]), "+v"(kv[1]), "+v"(kv[2]), "+v"(kv[3]), "+v"(kv[4]), "+v"(kv[5]),
-                     "+v"(kv[6]), "+v"(kv[7]), "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]),
-                     "+v"(va[4]), "+v"(va[5]), "+v"(va[6]), "+v"(va[7]), "+v"(va[8]), "+v"(va[9]),
-                     "+v"(va[10]), "+v"(va[11]), "+v"(va[12]), "+v"(va[13]), "+v"(va[14]),
-                     "+v"(va[15]));
+                   : "+v"(va[0]), "+v"(va[1]), "+v"(va[2]), "+v"(va[3]), "+v"(va[4]), "+v"(va[5]),
+                     "+v"(va[6]), "+v"(va[7]), "+v"(va[8]), "+v"(va[9]), "+v"(va[10]), "+v"(va[11]),
+                     "+v"(va[12]), "+v"(va[13]), "+v"(va[14]), "+v"(va[15])
+                   :
+                   : "memory");
+      const u32x4* kv = kreg[j];
       // S^T = K Q^T as two independent MFMA chains over d.
       f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -513,24 +518,34 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
         o[db] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, va[db]), pb, o[db], 0, 0, 0);
     };
 
-    // Two-stage pipeline.  Entering iteration u, steps u and (if it exists)
-    // u + 1 are in flight.
-    for (int u = la; u < lb; u += 2) {
-      if (u + 1 < lb) {
-        PA_WAIT_VMCNT(16);   // step u has landed; step u + 1 may be in flight
-      } else {
-        PA_WAIT_VMCNT(0);
+    // kStages-deep pipeline.  Before step i (relative to la) is computed,
+    // steps up to i + kStages - 1 have been issued; after it, step
+    // i + kStages goes into the slot it frees.  The steady loop always has
+    // kStages steps in flight (its issue is unconditional); the remaining
+    // steps are computed after it.  The waits for each step's registers are
+    // the compiler's (exact: every load in flight is a plain register load).
+    int i0 = 0;
+    if (deep) {
+#pragma unroll
+      for (int j = 0; j < kStages; ++j) issue(j);
+      for (; i0 + 2 * kStages <= nsteps; i0 += kStages) {
+#pragma unroll
+        for (int j = 0; j < kStages; ++j) {
+          compute(j);
+          issue(j);
+        }
       }
-      compute(0);
-      if (u + 1 >= lb) break;
-      if (u + 2 < lb) {
-        issue(stA);
-        PA_WAIT_VMCNT(16);
-      } else {
-        PA_WAIT_VMCNT(0);
-      }
-      compute(kStageBytes);
-      if (u + 3 < lb) issue(stB);
+    } else {
+#pragma unroll
+      for (int j = 0; j < kStages; ++j)
+        if (j < nsteps) issue(j);
+    }
+#pragma unroll
+    for (int j = 0; j < 2 * kStages - 1; ++j) {
+      const int i = i0 + j;
+      if (i >= nsteps) break;
+      compute(j % kStages);
+      if (i + kStages < nsteps) issue(j % kStages);
     }
     if (append_store) {
       const int64_t page_id = load_const_i32(bt + last_page);
