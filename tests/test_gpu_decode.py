@@ -220,3 +220,17 @@ def test_append_single_kv_head_shard():
     c = W.make_decode_case("append_hkv1", 11, [4097, 833], 832, 12, hkv=1, hq=6)
     log(c.name)
     _check_append(c)
+
+
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 9, 12])
+def test_steps_per_workgroup_sweep(n):
+    """One sequence whose 16-token steps give every split workgroup n or n + 1
+    steps, so the kernel's short path (all steps issued up front), its deep
+    path with and without a steady round, and the round boundaries all run;
+    both the two-call path and the appending launch."""
+    L = 4096 * n + 1600            # cached tokens; +1 appended
+    B = 832
+    pages = -(-(L + 1) // B)
+    c = W.make_decode_case(f"steps_per_wg_{n}", 300 + n, [L], B, pages + 3)
+    log(c.name)
+    _check_append(c)
