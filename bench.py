@@ -421,6 +421,52 @@ def cpu_baseline(case, seconds):
                       f"{el:.1f} s on the host CPU (fp64 NumPy oracle)"}
 
 
+def oracle_timings(W):
+    """The fp64 oracle on the other workloads, beside the GPU figures: one
+    32K-context decode step (page 832), one step of the 16-sequence batch
+    (timed on four of its sequences, scaled by K/V bytes), and
+    each prefill chunk on a sample of 256 query rows spread over the chunk,
+    scaled to the whole chunk by rows (a row's cost grows with its causal key
+    count; the sample's rows are evenly spaced, so their mean cost is the
+    chunk's).  Milliseconds of host time."""
+    import numpy as np
+    import oracle
+    out = {}
+    for name, case, sample in (("decode_ctx32768_b832", W.decode_32k(832), None),
+                               ("decode_batch16_ctx4k_32k_b832", W.batched_decode(), [0, 1, 2, 3])):
+        k, v = case.k_cache, case.v_cache
+        if len(case.positions):
+            slots = oracle.slot_mapping(case.positions, case.token_seq, case.block_tables,
+                                        case.block_size)
+            k, v = oracle.kv_write(k, v, case.k_new, case.v_new, slots)
+        t0 = time.perf_counter()
+        oracle.decode(case.q, k, v, case.block_tables, case.seq_lens, case.block_size, case.scale,
+                      seqs=sample)
+        el = time.perf_counter() - t0
+        if sample is None:
+            out[name] = {"ms_per_step": round(el * 1e3, 1)}
+        else:
+            frac = kv_bytes(case.seq_lens[sample]) / kv_bytes(case.seq_lens)
+            out[name] = {"ms_per_step_est": round(el * 1e3 / frac, 1),
+                         "sample": f"sequences {sample} ({el * 1e3:.1f} ms, {frac:.3f} of the "
+                                   f"K/V bytes), scaled by K/V bytes"}
+    case = W.prefill_8k()
+    for ch in case.chunks:
+        pos = np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64)
+        slots = oracle.slot_mapping(pos, None, case.block_table, case.block_size)
+        k, v = oracle.kv_write(case.k_cache, case.v_cache, ch.k_new, ch.v_new, slots)
+        rows = np.linspace(0, ch.q_len - 1, min(256, ch.q_len)).astype(np.int64)
+        K = oracle.gather_kv(k, case.block_table, ch.start_pos + ch.q_len, case.block_size)
+        V = oracle.gather_kv(v, case.block_table, ch.start_pos + ch.q_len, case.block_size)
+        t0 = time.perf_counter()
+        oracle.attend(ch.q[rows], ch.start_pos + rows, K, V, case.scale, causal=True)
+        el = time.perf_counter() - t0
+        out[f"prefill_q{ch.q_len}_start{ch.start_pos}"] = {
+            "ms_per_chunk_est": round(el * 1e3 * ch.q_len / len(rows), 1),
+            "sample": f"{len(rows)} of {ch.q_len} rows ({el * 1e3:.1f} ms), scaled by rows"}
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -478,6 +524,9 @@ def main():
     if not args.no_cpu:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         cpu = cpu_baseline(head_case, args.cpu_seconds)
+        if not args.no_extra:
+            print("[bench] oracle on the other workloads", file=sys.stderr, flush=True)
+            extra["oracle_ms"] = oracle_timings(W)
 
     achieved = head["kernel_gbs"]
     line = {
