@@ -66,9 +66,12 @@ constexpr int kTileBytes = 16 * kRowBytes;         // 16 V rows of one wave step
 constexpr int kMergeLds = kWaves * kGqa * (kHeadDim + 2) * 4;
 constexpr int kSmemBytes = kWaves * kTileBytes > kMergeLds ? kWaves * kTileBytes : kMergeLds;
 constexpr float kRescaleSlack = 8.f;               // log2 headroom before re-basing O
-constexpr int kMergeSlices = 32;                   // partials merged in parallel per dim
-constexpr int kMergeDims = 32;                     // dims per merge workgroup (one 128 B line)
-constexpr int kMergeParts = 8;                     // partials per merge thread
+#ifndef PA_MERGE_DIMS
+#define PA_MERGE_DIMS 32
+#endif
+constexpr int kMergeDims = PA_MERGE_DIMS;          // dims per merge workgroup (32: one 128 B line)
+constexpr int kMergeSlices = 1024 / kMergeDims;    // partials merged in parallel per dim
+constexpr int kMergeParts = 256 / kMergeSlices;    // partials per merge thread
 static_assert(kDecodeWorkgroups <= kMergeSlices * kMergeParts, "one merge round covers all partials");
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -627,10 +630,11 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
   }
 }
 
-// Merge of the partials: workgroup (query head h, 32-dim slice, sequence).
-// Thread t: slice z = t / 8 takes partials z, z + 32, ..., z + 224; it reads
-// dims 4*(t % 8) .. +3 of the slice, so eight threads read one partial's
-// 128-byte line of the slice.
+// Merge of the partials: workgroup (query head h, kMergeDims-dim slice,
+// sequence).  Thread t: slice z = t / (kMergeDims / 4) takes partials z,
+// z + kMergeSlices, ...; it reads dims 4*(t % (kMergeDims / 4)) .. +3 of the
+// slice, so with 32 dims eight threads read one partial's 128-byte line.
+// (Measured: 32 dims per workgroup beats 16 and 8.)
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float red_o[4][kMergeDims];
   __shared__ float red_m[4];
@@ -702,8 +706,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
     Ls += f * lv[k];
     O += f * av[k];
   }
-  // Combine the 32 slices: within a wave over lane bits 3..5 (slices
-  // 8w' .. 8w'+7), then the four waves' results through LDS.
+  // Combine the kMergeSlices slices: within a wave over the lane bits above
+  // the dim group, then the four waves' results through LDS.
   auto combine = [&](float M2, float L2, f32x4 O2) {
     const float Mn = fmaxf(M, M2);
     const float mu = Mn == -INFINITY ? 0.f : Mn;
@@ -713,7 +717,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
     M = Mn;
   };
 #pragma unroll
-  for (int off = 8; off < 64; off <<= 1) {
+  for (int off = kMergeDims / 4; off < 64; off <<= 1) {
     f32x4 O2;
 #pragma unroll
     for (int r = 0; r < 4; ++r) O2[r] = __shfl_xor(O[r], off);
