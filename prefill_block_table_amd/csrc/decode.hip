@@ -764,8 +764,8 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size
   const int64_t items = (int64_t)num_seqs * (num_kv_heads / p.heads_per_wg);
   const int64_t steps_ub = items * live_steps_host(max_seq_len, block_size, p.steps_per_page,
                                                    p.step_tokens);
-  // One split workgroup per CU (each holds 128 KB of LDS), never more
-  // workgroups than steps.
+  // One split workgroup per CU (its four waves take ~450 registers each, one
+  // wave per SIMD), never more workgroups than steps.
   int64_t n = kDecodeWorkgroups;
   if (n > steps_ub) n = steps_ub;
   p.num_wgs = (int32_t)n;

@@ -734,7 +734,7 @@ int tile_units(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_s
 
 PrefillPlan plan_prefill(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size,
                          int32_t num_kv_heads) {
-  // One workgroup per CU (128 KB of LDS each).  Items fill whole rounds of
+  // One workgroup per CU (160 KB of LDS each).  Items fill whole rounds of
   // kPrefillSlots workgroups heaviest first; the r items of an incomplete last
   // round (or all items, when there are fewer than the slots) are cut into
   // `split` parts so that round fills the CUs.  The lightest tile bounds the
