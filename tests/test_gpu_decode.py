@@ -234,3 +234,21 @@ def test_steps_per_workgroup_sweep(n):
     c = W.make_decode_case(f"steps_per_wg_{n}", 300 + n, [L], B, pages + 3)
     log(c.name)
     _check_append(c)
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_more_than_256_sequences(append):
+    """300 short sequences (1 to 700 tokens, page 64): the split kernel's scan
+    over more sequences than one workgroup has threads, and items that start
+    in one workgroup and end in another."""
+    rng = np.random.Generator(np.random.PCG64(77))
+    lens = [int(x) for x in rng.integers(1, 700, size=300)]
+    B = 64
+    pages = sum(-(-(n + 1) // B) for n in lens) + 3
+    c = W.make_decode_case(f"seqs300_{'append' if append else 'decode'}", 78, lens, B, pages,
+                           write_new_token=True)
+    log(c.name)
+    if append:
+        _check_append(c)
+    else:
+        compare(run_gpu(c), run_oracle(c), c.name)
