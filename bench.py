@@ -554,6 +554,7 @@ def main():
                      "launch_ms_avg": round(head["kernel_ms_avg"], 6),
                      "algorithmic_bytes_per_launch": head["kv_bytes"]},
         "cpu_baseline": cpu,
+        "build_info": pa.build_info(),
         "extra": extra,
     }
     print(json.dumps(line), flush=True)
