@@ -52,7 +52,7 @@
 namespace pa {
 
 const char* const kDecodeVariant =
-    "decode-v8(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-in-registers,3-steps-in-flight,"
+    "decode-v8(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-in-registers,3-steps-in-flight,nt-v,"
     "mfma16x16x32-qk,v-lds-transpose,tr16-vt,mfma16x16x16-pv,lazy-rescale,append)";
 
 namespace {
@@ -386,7 +386,11 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
     // Step issue into slot j: the 16 K rows of this wave go to kreg[j] (lane
     // (kq, c16) takes 16 bytes of row c16 per operand step: the MFMA A
     // operand as it is); the 16 V rows to vreg[j] (lane (half, pos) takes
-    // 16-byte chunk pos of rows 2*jj + half).
+    // 16-byte chunk pos of rows 2*jj + half).  V is read with streaming
+    // (non-temporal) loads, whole 512-byte rows per instruction; K with plain
+    // loads, since each K load covers only half of a 128-byte line and the
+    // next operand step reads the other half from L2 (streaming K loads were
+    // measured slower at 8K).
     auto issue = [&](const int j) __attribute__((always_inline)) {
       if (ip != ip_loaded) {
         ip_loaded = ip;
@@ -403,7 +407,7 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int t = 0; t < 8; ++t) kreg[j][t] = *reinterpret_cast<const u32x4*>(kp + 64 * t);
 #pragma unroll
-        for (int jj = 0; jj < 8; ++jj) vreg[j][jj] = *reinterpret_cast<const u32x4*>(vp + 2 * jj * rs_bytes);
+        for (int jj = 0; jj < 8; ++jj) vreg[j][jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp + 2 * jj * rs_bytes));
       } else {
         // Tail step: rows at or past lim reload the page's first row
         // (finite; masked out of the softmax) or, when appending, take
@@ -422,7 +426,7 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
           const bool fresh = key >= lim && append && ip == last_page;
           const char* vp = fresh ? vnew + 16 * pos
                                  : vcache + ip_base + (uint32_t)(key < lim ? key : 0) * rs_bytes + 16 * pos;
-          vreg[j][jj] = *reinterpret_cast<const u32x4*>(vp);
+          vreg[j][jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
         }
       }
       if (++isp == spp) { isp = 0; ++ip; }
