@@ -32,11 +32,14 @@
 //    - O^T is re-based to a new running max only when a score exceeds the
 //      current reference by more than 2^8 (exact; keeps the accumulator out
 //      of the VALU on almost every step).
-//    Each (item, workgroup) pair that shares work leaves one partial (m, l,
-//    unnormalised O) per KV head; an item done by a single workgroup writes
-//    bf16 output directly.
+//    Each (item, workgroup) pair that shares work leaves one partial per KV
+//    head: the running max m and sum l in fp32 and the normalised O / l in
+//    bf16 (half the bytes of fp32 on both sides of the kernel boundary; one
+//    more bf16 rounding than the single-workgroup path, whose O / l is the
+//    output itself); an item done by a single workgroup writes bf16 output
+//    directly.
 // 2. decode_merge_kernel.  One workgroup per (sequence, query head, 32-dim
-//    slice: one 128-byte line of a partial); its 256 threads load all (at
+//    slice of a partial); its 256 threads load all (at
 //    most 256) partials of the slice in one round, so every load of a
 //    workgroup is in flight at once, then combine them with cross-lane
 //    shuffles.  Merge order is fixed: results are bitwise repeatable, no
@@ -52,10 +55,12 @@
 namespace pa {
 
 const char* const kDecodeVariant =
-    "decode-v8(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-in-registers,3-steps-in-flight,nt-v,"
+    "decode-v8(split+merge,balanced-steps,4heads-per-wg,16tok-steps,kv-in-registers,3-steps-in-flight,nt-v,bf16-partials,"
     "mfma16x16x32-qk,v-lds-transpose,tr16-vt,mfma16x16x16-pv,lazy-rescale,append)";
 
 namespace {
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
 constexpr int kStages = 3;                         // steps in flight per wave
@@ -69,7 +74,7 @@ constexpr float kRescaleSlack = 8.f;               // log2 headroom before re-ba
 #ifndef PA_MERGE_DIMS
 #define PA_MERGE_DIMS 32
 #endif
-constexpr int kMergeDims = PA_MERGE_DIMS;          // dims per merge workgroup (32: one 128 B line)
+constexpr int kMergeDims = PA_MERGE_DIMS;          // dims per merge workgroup (32: 64 contiguous bytes of a bf16 partial)
 constexpr int kMergeSlices = 1024 / kMergeDims;    // partials merged in parallel per dim
 constexpr int kMergeParts = 256 / kMergeSlices;    // partials per merge thread
 static_assert(kDecodeWorkgroups <= kMergeSlices * kMergeParts, "one merge round covers all partials");
@@ -96,7 +101,7 @@ struct DecodeArgs {
   int32_t step_tokens;     // 16 * (4 / heads_per_wg)
   int32_t steps_per_page;
   int32_t num_wgs;         // split workgroups (grid of the split kernel)
-  float* p_acc;            // [slot][heads_per_wg][6][256], slot = item + workgroup
+  uint16_t* p_acc;         // [slot][heads_per_wg][6][256] bf16 O / l, slot = item + workgroup
   float* p_ml;             // [slot][heads_per_wg][6][2]
   int32_t* meta;           // [item][2]: first workgroup, number of partials
   // Appended token (NULL k_new: plain decode).  Row [s][g] of k_new / v_new
@@ -616,13 +621,15 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
         }
       } else {
         const int64_t slot = (int64_t)item + wgi;
-        float* pacc = a.p_acc + (slot * HPW + jw) * (kGqa * kHeadDim) + c16 * kHeadDim + 4 * kq;
+        const float inv = 1.f / l_run;
+        uint16_t* pacc = a.p_acc + (slot * HPW + jw) * (kGqa * kHeadDim) + c16 * kHeadDim + 4 * kq;
 #pragma unroll
-        for (int db = 0; db < 16; ++db) *reinterpret_cast<f32x4*>(pacc + 16 * db) = o[db];
-        if (kq == 0) {
-          a.p_ml[(slot * HPW + jw) * (kGqa * 2) + 2 * c16] = m_run;
-          a.p_ml[(slot * HPW + jw) * (kGqa * 2) + 2 * c16 + 1] = l_run;
+        for (int db = 0; db < 16; ++db) {
+          const u32x2 v = {pack_bf16x2(o[db][0] * inv, o[db][1] * inv), pack_bf16x2(o[db][2] * inv, o[db][3] * inv)};
+          *reinterpret_cast<u32x2*>(pacc + 16 * db) = v;
         }
+        if (kq == 0)
+          *reinterpret_cast<f32x2*>(a.p_ml + (slot * HPW + jw) * (kGqa * 2) + 2 * c16) = f32x2{m_run, l_run};
       }
     }
     if (tid == 0 && first_wg == wgi) {
@@ -637,7 +644,7 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
 // Merge of the partials: workgroup (query head h, kMergeDims-dim slice,
 // sequence).  Thread t: slice z = t / (kMergeDims / 4) takes partials z,
 // z + kMergeSlices, ...; it reads dims 4*(t % (kMergeDims / 4)) .. +3 of the
-// slice, so with 32 dims eight threads read one partial's 128-byte line.
+// slice, so with 32 dims eight threads read one partial slice (64 bytes of bf16).
 // (Measured: 32 dims per workgroup beats 16 and 8.)
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float red_o[4][kMergeDims];
@@ -669,18 +676,17 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   constexpr int kParts = kMergeParts;
   const int64_t pml = (int64_t)hpw * (kGqa * 2);          // stride between consecutive slots
   const int64_t pacc = (int64_t)hpw * (kGqa * kHeadDim);
-  float mv[kParts], lv[kParts];
-  f32x4 av[kParts];
+  f32x2 mlv[kParts];
+  u32x2 av[kParts];
   auto load_parts = [&](int64_t slot0, int count) {
     const float* ml = a.p_ml + (slot0 * hpw + jw) * (kGqa * 2) + 2 * hh;
-    const float* acc = a.p_acc + (slot0 * hpw + jw) * (kGqa * kHeadDim) + hh * kHeadDim + d;
+    const uint16_t* acc = a.p_acc + (slot0 * hpw + jw) * (kGqa * kHeadDim) + hh * kHeadDim + d;
 #pragma unroll
     for (int k = 0; k < kParts; ++k) {
       const int p = z + k * kMergeSlices;
       const bool ok = p < count;
-      mv[k] = ok ? ml[p * pml] : -INFINITY;
-      lv[k] = ok ? ml[p * pml + 1] : 0.f;
-      av[k] = ok ? *reinterpret_cast<const f32x4*>(acc + p * pacc) : f32x4{0.f, 0.f, 0.f, 0.f};
+      mlv[k] = ok ? *reinterpret_cast<const f32x2*>(ml + p * pml) : f32x2{-INFINITY, 0.f};
+      av[k] = ok ? *reinterpret_cast<const u32x2*>(acc + p * pacc) : u32x2{0u, 0u};
     }
   };
   load_parts(item, a.num_wgs);
@@ -696,19 +702,19 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   if (first != 0) load_parts((int64_t)item + first, nparts);
 #pragma unroll
   for (int k = 0; k < kParts; ++k) {
-    if (z + k * kMergeSlices >= nparts) { mv[k] = -INFINITY; lv[k] = 0.f; av[k] = f32x4{0.f, 0.f, 0.f, 0.f}; }
+    if (z + k * kMergeSlices >= nparts) { mlv[k] = f32x2{-INFINITY, 0.f}; av[k] = u32x2{0u, 0u}; }
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int k = 0; k < kParts; ++k) M = fmaxf(M, mv[k]);
+  for (int k = 0; k < kParts; ++k) M = fmaxf(M, mlv[k][0]);
   const float mu = M == -INFINITY ? 0.f : M;
   float Ls = 0.f;
   f32x4 O = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < kParts; ++k) {
-    const float f = fast_exp2(mv[k] - mu);
-    Ls += f * lv[k];
-    O += f * av[k];
+    const float f = fast_exp2(mlv[k][0] - mu) * mlv[k][1];
+    Ls += f;
+    O += f * f32x4{bf16_lo(av[k][0]), bf16_hi(av[k][0]), bf16_lo(av[k][1]), bf16_hi(av[k][1])};
   }
   // Combine the kMergeSlices slices: within a wave over the lane bits above
   // the dim group, then the four waves' results through LDS.
@@ -778,7 +784,7 @@ DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size
   size_t off = 0;
   p.meta_off = off;  off += align256((size_t)items * 2 * sizeof(int32_t));
   p.p_ml_off = off;  off += align256(slots * p.heads_per_wg * kGqa * 2 * sizeof(float));
-  p.p_acc_off = off; off += align256(slots * p.heads_per_wg * kGqa * kHeadDim * sizeof(float));
+  p.p_acc_off = off; off += align256(slots * p.heads_per_wg * kGqa * kHeadDim * sizeof(uint16_t));
   p.bytes = off;
   return p;
 }
@@ -811,7 +817,7 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   a.num_wgs = plan.num_wgs;
   a.meta = reinterpret_cast<int32_t*>(ws + plan.meta_off);
   a.p_ml = reinterpret_cast<float*>(ws + plan.p_ml_off);
-  a.p_acc = reinterpret_cast<float*>(ws + plan.p_acc_off);
+  a.p_acc = reinterpret_cast<uint16_t*>(ws + plan.p_acc_off);
   a.k_new = append ? append->k_new : nullptr;
   a.v_new = append ? append->v_new : nullptr;
   a.k_dst = append ? append->k_cache : nullptr;

@@ -57,6 +57,19 @@ def test_decode_8k_with_slot_mapping_write():
     compare(run_gpu(c), run_oracle(c), c.name)
 
 
+@pytest.mark.parametrize("q_gain", [4.0, 16.0])
+def test_peaked_attention_8k(q_gain):
+    """q scaled by a power of two (exact in bf16), so the score spread grows
+    to several times, then sixteen times, the workload's: each workgroup's
+    partial is dominated by a few rows, the running max is re-based often,
+    and the merge weighs partials whose maxima differ by hundreds (log2
+    units).  The bf16 partials and the merge must stay within tolerance."""
+    c = W.decode_8k(seed=12)
+    c.q = W.f32_to_bf16_bits((oracle.bf16_bits_to_f64(c.q) * q_gain).astype(np.float32))
+    log(f"{c.name} q x {q_gain}")
+    compare(run_gpu(c), run_oracle(c), f"{c.name} q x {q_gain}")
+
+
 @pytest.mark.parametrize("B", [784, 832, 1024])
 def test_decode_32k_page_sweep(B):
     c = W.decode_32k(B)
