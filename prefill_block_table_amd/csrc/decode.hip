@@ -76,6 +76,7 @@ constexpr float kRescaleSlack = 8.f;               // log2 headroom before re-ba
 #endif
 constexpr int kMergeDims = PA_MERGE_DIMS;          // dims per merge workgroup (32: 64 contiguous bytes of a bf16 partial)
 constexpr int kMergeSlices = 1024 / kMergeDims;    // partials merged in parallel per dim
+constexpr int kLineSlices = kMergeDims >= 64 ? 1 : 64 / kMergeDims;   // merge slices per 128 B line
 constexpr int kMergeParts = 256 / kMergeSlices;    // partials per merge thread
 static_assert(kDecodeWorkgroups <= kMergeSlices * kMergeParts, "one merge round covers all partials");
 
@@ -650,8 +651,15 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float red_o[4][kMergeDims];
   __shared__ float red_m[4];
   __shared__ float red_l[4];
-  const int h = blockIdx.x / (kHeadDim / kMergeDims);
-  const int dc = blockIdx.x % (kHeadDim / kMergeDims);
+  // Workgroups go round-robin to the 8 XCDs (id % 8) and each XCD has its own
+  // L2, so the kLineSlices slices that share a 128-byte line of a partial
+  // are given ids with the same id % 8: each line is then fetched by one L2.
+  // gridDim.x = Hq * kHeadDim / kMergeDims is a multiple of 8 * kLineSlices.
+  const int xcd = blockIdx.x % 8;
+  const int q8 = blockIdx.x / 8;
+  const int slice = (q8 / kLineSlices * 8 + xcd) * kLineSlices + q8 % kLineSlices;
+  const int h = slice / (kHeadDim / kMergeDims);
+  const int dc = slice % (kHeadDim / kMergeDims);
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
   const int z = tid / (kMergeDims / 4);
