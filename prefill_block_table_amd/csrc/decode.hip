@@ -15,8 +15,9 @@
 //    flattened step list is cut into one near-equal contiguous range per
 //    workgroup, about one workgroup per CU, so short and long sequences of a
 //    batch are balanced.  Per wave and step:
-//    - K and V rows go from HBM into registers with plain 16-byte loads,
-//      three steps in flight per wave: each lane's K loads are exactly its
+//    - K and V rows go from HBM into registers with 16-byte loads (V's with
+//      the streaming hint: each V load covers whole 128-byte lines read
+//      once), three steps in flight per wave: each lane's K loads are exactly its
 //      MFMA A operand (row = key, 8 consecutive dims), so K never touches
 //      LDS; V rows pass through a wave-private LDS tile (16-byte chunks
 //      XOR-swizzled by row, so the transposing reads below are bank-conflict
@@ -39,10 +40,10 @@
 //    output itself); an item done by a single workgroup writes bf16 output
 //    directly.
 // 2. decode_merge_kernel.  One workgroup per (sequence, query head, 32-dim
-//    slice of a partial); its 256 threads load all (at
-//    most 256) partials of the slice in one round, so every load of a
-//    workgroup is in flight at once, then combine them with cross-lane
-//    shuffles.  Merge order is fixed: results are bitwise repeatable, no
+//    slice of a partial); its 256 threads load all (at most 256) partials of
+//    the slice in one round, so every load of a workgroup is in flight at
+//    once, then combine them with cross-lane shuffles.  The two slices that
+//    share a 128-byte line run on one XCD, so each line is fetched once.  Merge order is fixed: results are bitwise repeatable, no
 //    atomics anywhere.
 // Nothing is read past a page's or a sequence's last live row (such rows are
 // replaced by the page's first row, whose weight is exactly 0), so poisoned
