@@ -391,6 +391,48 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   u32x4 pcur[2] = {{0u, 0u, 0u, 0u}, {0u, 0u, 0u, 0u}};
   uint32_t pv_vbase = 0;
 
+  // O^T += V^T P^T for the group whose P is pbv and whose V tile starts at vbase
+  // (this wave's key half): V^T operands come from transposing LDS reads one
+  // batch of two d-blocks ahead of the MFMAs.
+  auto pv = [&](const u32x4 (&pbv)[2], const uint32_t vbase) {
+    u32x2 va[2][2][2];
+    // batch b: d-blocks 2*b, 2*b + 1
+    auto vread = [&](int b, u32x2 (&d)[2][2]) {
+      switch (b) {
+#define PA_VR(BB)                                                                        \
+  case BB: {                                                                             \
+    constexpr int db0 = 2 * (BB), db1 = 2 * (BB) + 1;                                    \
+    const uint32_t a0 = vbase ^ ((db0 & 7) << 5), a1 = vbase ^ ((db1 & 7) << 5);         \
+    PA_DS_READ_TR16(d[0][0], a0, 256 * (db0 >> 3));                                      \
+    PA_DS_READ_TR16(d[0][1], a0, 256 * (db0 >> 3) + 16 * kRowBytes);                     \
+    PA_DS_READ_TR16(d[1][0], a1, 256 * (db1 >> 3));                                      \
+    PA_DS_READ_TR16(d[1][1], a1, 256 * (db1 >> 3) + 16 * kRowBytes);                     \
+  } break;
+        PA_VR(0) PA_VR(1) PA_VR(2) PA_VR(3) PA_VR(4) PA_VR(5) PA_VR(6) PA_VR(7)
+#undef PA_VR
+      }
+    };
+    vread(0, va[0]);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const int cur = b & 1;
+      if (b < 7) {
+        vread(b + 1, va[cur ^ 1]);
+        asm volatile("s_waitcnt lgkmcnt(4)"
+                     : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
+      } else {
+        asm volatile("s_waitcnt lgkmcnt(0)"
+                     : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pbv[rb], o[2 * b + t][rb]);
+      }
+    }
+  };
+
   int cp = ga / upp, cg = ga % upp;        // compute cursor (page, group)
   // One barrier per group.  Waves w and w + 4 share a SIMD.  Waves 0..3 run
   // each group as scores, softmax, PV; waves 4..7 run the PV of a group at
@@ -410,44 +452,6 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     PA_WAIT_VMCNT(0);
     PA_BARRIER();
     const bool more = u + 1 < gb;
-    auto pv = [&](const u32x4 (&pbv)[2], const uint32_t vbase) {
-      u32x2 va[2][2][2];
-      // batch b: d-blocks 2*b, 2*b + 1
-      auto vread = [&](int b, u32x2 (&d)[2][2]) {
-        switch (b) {
-#define PA_VR(BB)                                                                        \
-  case BB: {                                                                             \
-    constexpr int db0 = 2 * (BB), db1 = 2 * (BB) + 1;                                    \
-    const uint32_t a0 = vbase ^ ((db0 & 7) << 5), a1 = vbase ^ ((db1 & 7) << 5);         \
-    PA_DS_READ_TR16(d[0][0], a0, 256 * (db0 >> 3));                                      \
-    PA_DS_READ_TR16(d[0][1], a0, 256 * (db0 >> 3) + 16 * kRowBytes);                     \
-    PA_DS_READ_TR16(d[1][0], a1, 256 * (db1 >> 3));                                      \
-    PA_DS_READ_TR16(d[1][1], a1, 256 * (db1 >> 3) + 16 * kRowBytes);                     \
-  } break;
-          PA_VR(0) PA_VR(1) PA_VR(2) PA_VR(3) PA_VR(4) PA_VR(5) PA_VR(6) PA_VR(7)
-#undef PA_VR
-        }
-      };
-      vread(0, va[0]);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int cur = b & 1;
-        if (b < 7) {
-          vread(b + 1, va[cur ^ 1]);
-          asm volatile("s_waitcnt lgkmcnt(4)"
-                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pbv[rb], o[2 * b + t][rb]);
-        }
-      }
-    };
 
     auto qksm = [&]() {
       const int key0 = cp * B + cg * kGroup;
@@ -571,45 +575,6 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     }
   }
   if (w >= 4 && pv_go) {
-    auto pv = [&](const u32x4 (&pbv)[2], const uint32_t vbase) {
-      u32x2 va[2][2][2];
-      // batch b: d-blocks 2*b, 2*b + 1
-      auto vread = [&](int b, u32x2 (&d)[2][2]) {
-        switch (b) {
-#define PA_VR(BB)                                                                        \
-  case BB: {                                                                             \
-    constexpr int db0 = 2 * (BB), db1 = 2 * (BB) + 1;                                    \
-    const uint32_t a0 = vbase ^ ((db0 & 7) << 5), a1 = vbase ^ ((db1 & 7) << 5);         \
-    PA_DS_READ_TR16(d[0][0], a0, 256 * (db0 >> 3));                                      \
-    PA_DS_READ_TR16(d[0][1], a0, 256 * (db0 >> 3) + 16 * kRowBytes);                     \
-    PA_DS_READ_TR16(d[1][0], a1, 256 * (db1 >> 3));                                      \
-    PA_DS_READ_TR16(d[1][1], a1, 256 * (db1 >> 3) + 16 * kRowBytes);                     \
-  } break;
-          PA_VR(0) PA_VR(1) PA_VR(2) PA_VR(3) PA_VR(4) PA_VR(5) PA_VR(6) PA_VR(7)
-#undef PA_VR
-        }
-      };
-      vread(0, va[0]);
-#pragma unroll
-      for (int b = 0; b < 8; ++b) {
-        const int cur = b & 1;
-        if (b < 7) {
-          vread(b + 1, va[cur ^ 1]);
-          asm volatile("s_waitcnt lgkmcnt(4)"
-                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
-        } else {
-          asm volatile("s_waitcnt lgkmcnt(0)"
-                       : "+v"(va[cur][0][0]), "+v"(va[cur][0][1]), "+v"(va[cur][1][0]), "+v"(va[cur][1][1]));
-        }
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const u32x4 av = {va[cur][t][0][0], va[cur][t][0][1], va[cur][t][1][0], va[cur][t][1][1]};
-#pragma unroll
-          for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pbv[rb], o[2 * b + t][rb]);
-        }
-      }
-    };
-
     pv(pcur, pv_vbase);
   }
 
