@@ -61,8 +61,6 @@ const char* const kDecodeVariant =
 
 namespace {
 
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int kWaves = 4;
 constexpr int kStages = 3;                         // steps in flight per wave
 constexpr int kRowBytes = kHeadDim * 2;            // one KV head's row: 512 B

@@ -11,6 +11,7 @@ constexpr int kGqa = 6;         // query heads per KV head ([ALIGN] §4)
 constexpr int kGroup = 64;      // tokens per access group ([ALIGN] §2)
 
 typedef __attribute__((__vector_size__(8 * sizeof(__bf16)))) __bf16 bf16x8;
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((__vector_size__(4 * sizeof(float)))) float f32x4;
 typedef __attribute__((__vector_size__(16 * sizeof(float)))) float f32x16;
 typedef __attribute__((__vector_size__(4 * sizeof(uint32_t)))) uint32_t u32x4;

@@ -92,7 +92,7 @@ struct PrefillArgs {
   // ranges whose partial results go to part_o / part_ml.
   int32_t num_full;
   int32_t split;
-  float* part_o;           // [slot][128 rows][256], slot = (item - num_full) * split + part
+  uint16_t* part_o;        // [slot][128 rows][256] bf16 O / l, slot = (item - num_full) * split + part
   float* part_ml;          // [slot][128 rows][2]: row max (log2 units), row sum
   // Several sequences (pa_prefill_varlen; NULL cu_seqlens_q: one sequence,
   // q_len / start_pos / block_table above): sequence s has query rows
@@ -620,18 +620,21 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         if (row < q_len) {
           const int64_t slot = (int64_t)(item - a.num_full) * a.split + part;
           const int trow = row - q0;
-          float* po = a.part_o + (slot * kBM + trow) * kHeadDim + 4 * (lane_e >> 4);
+          // The part's O / l in bf16 (zero for a row with no key in the
+          // part: l = 0 there, and the merge gives it weight 0).
+          const float pinv = lsum > 0.f ? 1.f / lsum : 0.f;
+          const float wa = f * pinv, wb = fp * pinv;
+          uint16_t* po = a.part_o + (slot * kBM + trow) * kHeadDim + 4 * (lane_e >> 4);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const f32x4 x = o[8 * mine + j][rb];
             const f32x4 y = xo_peer[(rb * 8 + j) * 64 + lane_e];
-            *reinterpret_cast<f32x4*>(po + 16 * (8 * mine + j)) =
-                f32x4{x[0] * f + y[0] * fp, x[1] * f + y[1] * fp, x[2] * f + y[2] * fp, x[3] * f + y[3] * fp};
+            *reinterpret_cast<u32x2*>(po + 16 * (8 * mine + j)) =
+                u32x2{pack_bf16x2(x[0] * wa + y[0] * wb, x[1] * wa + y[1] * wb),
+                      pack_bf16x2(x[2] * wa + y[2] * wb, x[3] * wa + y[3] * wb)};
           }
-          if (mine == 0 && (lane_e >> 4) == 0) {
-            a.part_ml[(slot * kBM + trow) * 2] = M;
-            a.part_ml[(slot * kBM + trow) * 2 + 1] = lsum;
-          }
+          if (mine == 0 && (lane_e >> 4) == 0)
+            *reinterpret_cast<f32x2*>(a.part_ml + (slot * kBM + trow) * 2) = f32x2{M, lsum};
         }
         continue;
       }
@@ -676,10 +679,11 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int k = 0; k < a.split; ++k) {
     const int64_t slot = (int64_t)item_idx * a.split + k;
-    const float f = fast_exp2(a.part_ml[(slot * kBM + trow) * 2] - M);
-    lsum += f * a.part_ml[(slot * kBM + trow) * 2 + 1];
-    const f32x4 v = *reinterpret_cast<const f32x4*>(a.part_o + (slot * kBM + trow) * kHeadDim + d);
-    acc += f * v;
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.part_ml + (slot * kBM + trow) * 2);
+    const float f = fast_exp2(ml[0] - M) * ml[1];   // weight of the part's O / l
+    lsum += f;
+    const u32x2 v = *reinterpret_cast<const u32x2*>(a.part_o + (slot * kBM + trow) * kHeadDim + d);
+    acc += f * f32x4{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
   }
   const float inv = 1.f / lsum;
   const int64_t q_stride = (int64_t)a.num_kv_heads * kGqa * kHeadDim;
@@ -719,7 +723,7 @@ PrefillPlan plan_prefill(int32_t q_len, int32_t start_pos, int32_t causal, int32
   p.split_items = r;
   const size_t slots = (size_t)(r * (S > 1 ? S : 0));
   p.part_o_off = 0;
-  p.part_ml_off = (slots * kBM * kHeadDim * sizeof(float) + 255) & ~(size_t)255;
+  p.part_ml_off = (slots * kBM * kHeadDim * sizeof(uint16_t) + 255) & ~(size_t)255;
   p.bytes = slots ? p.part_ml_off + ((slots * kBM * 2 * sizeof(float) + 255) & ~(size_t)255) : 0;
   return p;
 }
@@ -753,7 +757,7 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   a.max_q = q_len;
   a.max_k = start_pos + q_len;
   char* ws = static_cast<char*>(workspace);
-  a.part_o = plan.bytes ? reinterpret_cast<float*>(ws + plan.part_o_off) : nullptr;
+  a.part_o = plan.bytes ? reinterpret_cast<uint16_t*>(ws + plan.part_o_off) : nullptr;
   a.part_ml = plan.bytes ? reinterpret_cast<float*>(ws + plan.part_ml_off) : nullptr;
   const int64_t grid = plan.num_full + plan.split_items * plan.split;
   hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kWavesPf * 64), 0, stream, a);

@@ -120,12 +120,15 @@ def test_single_kv_head_shard():
 # the last round are cut along their key groups and combined by a second
 # launch (q=128 @ 8192: 24 items, 10 parts each; q=1 @ 32767: 24 items of one
 # row; q=300 @ 5000 on page 16: 72 items, 3 parts; q=1685 @ 8192 is covered by
-# the 8K test above).
+# the 8K test above).  q=128 @ 0: 2 parts of one key group each, so under the
+# causal mask rows 0..63 have no key in the second part (its partial for them
+# has l = 0 and must get weight 0, not NaN).
 SPLIT = [
     (832, 8192, 128),
     (784, 32767, 1),
     (16, 5000, 300),
     (1024, 2000, 640),
+    (832, 0, 128),
 ]
 
 
