@@ -235,6 +235,21 @@ def test_append_single_kv_head_shard():
     _check_append(c)
 
 
+@pytest.mark.parametrize("hkv", [2, 3, 6, 8, 64])
+def test_kv_head_counts(hkv):
+    """KV-head counts the ABI takes besides 1 and 4: an item holds 4 KV heads
+    when hkv % 4 == 0 (8 and 64: several items per sequence), 2 when
+    hkv % 4 == 2 (two waves per head, each taking half of every step, merged
+    through LDS), 1 otherwise (four waves per head); decode, the appending
+    launch and the two-call path, with a one-token sequence among them."""
+    lens = [2500, 517, 1] if hkv < 64 else [700, 33]
+    B = 64
+    pages = sum(-(-(n + 1) // B) for n in lens)
+    c = W.make_decode_case(f"hkv{hkv}", 300 + hkv, lens, B, pages + 3, hkv=hkv, hq=6 * hkv)
+    log(f"{c.name} lens={lens}")
+    _check_append(c)
+
+
 @pytest.mark.parametrize("n", [1, 2, 3, 4, 5, 6, 7, 9, 12])
 def test_steps_per_workgroup_sweep(n):
     """One sequence whose 16-token steps give every split workgroup n or n + 1

@@ -116,6 +116,17 @@ def test_single_kv_head_shard():
     compare(got[0], ref[0], c.name)
 
 
+@pytest.mark.parametrize("hkv", [2, 3, 8])
+def test_kv_head_counts(hkv):
+    """Other KV-head counts: the workgroup-to-item map groups the 6 query heads
+    of each KV head on one XCD for any count."""
+    c = W.make_prefill_case(f"hkv{hkv}", 80 + hkv, [(300, 260)], 832, 4, hkv=hkv, hq=6 * hkv)
+    log(c.name)
+    got = run_chunks_gpu(c)
+    ref = run_chunks_oracle(c)
+    compare(got[0], ref[0], c.name)
+
+
 # Chunks whose items do not fill whole rounds of 256 workgroups: the items of
 # the last round are cut along their key groups and combined by a second
 # launch (q=128 @ 8192: 24 items, 10 parts each; q=1 @ 32767: 24 items of one
