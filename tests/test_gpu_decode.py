@@ -280,3 +280,26 @@ def test_more_than_256_sequences(append):
         _check_append(c)
     else:
         compare(run_gpu(c), run_oracle(c), c.name)
+
+
+RANDOM_CASES = 16
+
+
+@pytest.mark.parametrize("i", range(RANDOM_CASES))
+def test_random_shapes(i):
+    """Seeded random shapes: page size (measured ones, odd ones, 1), KV-head
+    count, 1-6 sequences of 1-6000 tokens, with or without the appended token."""
+    rng = np.random.default_rng(5000 + i)
+    B = int(rng.choice([1, 3, 16, 64, 100, 784, 832, 1024, int(rng.integers(2, 1200))]))
+    hkv = int(rng.choice([1, 2, 3, 4, 4, 5, 6, 8]))
+    S = int(rng.integers(1, 7))
+    lens = [int(x) for x in rng.integers(1, 6001, size=S)]
+    append = bool(rng.integers(0, 2))
+    pages = sum(-(-(n + 1) // B) for n in lens) + 2
+    c = W.make_decode_case(f"rand{i}_b{B}_hkv{hkv}", 6000 + i, lens, B, pages,
+                           write_new_token=append, hkv=hkv, hq=6 * hkv)
+    log(f"{c.name} lens={lens} append={append}")
+    if append:
+        _check_append(c)
+    else:
+        compare(run_gpu(c), run_oracle(c), c.name)

@@ -196,3 +196,29 @@ def test_varlen_all_rows(idx, causal):
     _sync()
     ref = oracle.prefill_varlen(q, cu, used, causal, kh, vh, c.block_tables, B, c.scale)
     compare(bits(out), ref, c.name)
+
+
+RANDOM_CASES = 12
+
+
+@pytest.mark.parametrize("i", range(RANDOM_CASES))
+def test_random_shapes(i):
+    """Seeded random chunks: page size, KV-head count, start 0-2500, one or two
+    contiguous chunks of 1-700 rows, causal or not; every row checked."""
+    rng = np.random.default_rng(7000 + i)
+    B = int(rng.choice([1, 16, 64, 100, 784, 832, 1024, int(rng.integers(2, 1200))]))
+    hkv = int(rng.choice([1, 2, 3, 4, 4]))
+    start = int(rng.integers(0, 2501))
+    n1 = int(rng.integers(1, 701))
+    chunks = [(start, n1)]
+    if rng.integers(0, 2):
+        chunks.append((start + n1, int(rng.integers(1, 701))))
+    causal = bool(rng.integers(0, 4))          # mostly causal
+    end = chunks[-1][0] + chunks[-1][1]
+    c = W.make_prefill_case(f"rand{i}_b{B}_hkv{hkv}", 8000 + i, chunks, B, -(-end // B) + 2,
+                            causal=causal, hkv=hkv, hq=6 * hkv)
+    log(f"{c.name} chunks={chunks} causal={causal}")
+    got = run_chunks_gpu(c)
+    ref = run_chunks_oracle(c)
+    for j, (g, r) in enumerate(zip(got, ref)):
+        compare(g, r, f"{c.name}[{j}]")
