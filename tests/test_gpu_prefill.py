@@ -170,12 +170,35 @@ VARLEN = [
 @pytest.mark.parametrize("causal", [True, False])
 @pytest.mark.parametrize("idx", range(len(VARLEN)))
 def test_varlen_all_rows(idx, causal):
-    import torch
-    pa = _pa()
     B, seqs = VARLEN[idx]
     pages = sum(-(-(s0 + n) // B) for s0, n in seqs)
     c = W.make_varlen_prefill_case(f"varlen{idx}_b{B}", 80 + idx, seqs, B, pages + 4, causal=causal)
     log(f"{c.name} seqs={seqs} causal={causal}")
+    _check_varlen(c, causal)
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_varlen_random_shapes(i):
+    """Seeded random batches: 1-6 sequences, each at a random start with 0-400
+    rows, random page size and KV-head count, mostly causal."""
+    rng = np.random.default_rng(9000 + i)
+    B = int(rng.choice([1, 16, 64, 784, 832, 1024, int(rng.integers(2, 1200))]))
+    hkv = int(rng.choice([1, 2, 3, 4]))
+    seqs = [(int(rng.integers(0, 2001)), int(rng.integers(0, 401))) for _ in range(int(rng.integers(1, 7)))]
+    seqs = [(max(s0, 1) if n == 0 else s0, n) for s0, n in seqs]     # every sequence holds a token
+    if all(n == 0 for _, n in seqs):
+        seqs[0] = (seqs[0][0], 1)
+    causal = bool(rng.integers(0, 4))
+    B_pages = sum(-(-(s0 + n) // B) for s0, n in seqs)
+    c = W.make_varlen_prefill_case(f"varlen_rand{i}_b{B}_hkv{hkv}", 9500 + i, seqs, B, B_pages + 4,
+                                   causal=causal, hkv=hkv, hq=6 * hkv)
+    log(f"{c.name} seqs={seqs} causal={causal}")
+    _check_varlen(c, causal)
+
+
+def _check_varlen(c, causal):
+    pa = _pa()
+    B = c.block_size
     k, v = to_dev(c.k_cache), to_dev(c.v_cache)
     bt = to_dev(c.block_tables)
     kh, vh = c.k_cache, c.v_cache
