@@ -303,3 +303,20 @@ def test_random_shapes(i):
         _check_append(c)
     else:
         compare(run_gpu(c), run_oracle(c), c.name)
+
+
+def test_seq_lens_clamped_to_range():
+    """Lengths outside [0, max_seq_len] are clamped: a negative one gives an
+    all-zero output, one above max_seq_len attends the first max_seq_len keys,
+    and the other sequences are unaffected."""
+    pa = _pa()
+    c = W.make_decode_case("clamp", 41, [1, 2500, 700], 64, 4 + 40 + 11 + 3, write_new_token=False)
+    ref = run_oracle(c)                     # lengths 1, 2500, 700
+    lens = np.array([-5, 3000, 700], dtype=np.int32)
+    log(f"{c.name} seq_lens={lens.tolist()} max_seq_len=2500")
+    out = pa.decode(to_dev(c.q), to_dev(c.k_cache), to_dev(c.v_cache), to_dev(c.block_tables),
+                    to_dev(lens), 2500, c.scale)
+    _sync()
+    got = bits(out)
+    assert np.all(got[0] == 0)
+    compare(got[1:], ref[1:], c.name)
