@@ -245,3 +245,39 @@ def test_random_shapes(i):
     ref = run_chunks_oracle(c)
     for j, (g, r) in enumerate(zip(got, ref)):
         compare(g, r, f"{c.name}[{j}]")
+
+
+def test_varlen_short_keys_unwritten_and_long_keys_clamped():
+    """pa_prefill_varlen edge rules: a sequence given fewer keys than rows is
+    left unwritten (its rows keep the caller's poison), and a key count above
+    max_seqlen_k is clamped to it (the rows then sit at the last q_len of the
+    first max_seqlen_k positions); a normal sequence beside them is exact."""
+    import torch
+    pa = _pa()
+    B = 64
+    seqs = [(300, 200), (0, 10), (700, 100)]          # A, B (keys cut to 5 below), C (800 keys)
+    pages = sum(-(-(s0 + n) // B) for s0, n in seqs)
+    c = W.make_varlen_prefill_case("varlen_edges", 95, seqs, B, pages + 4, causal=True)
+    k, v = to_dev(c.k_cache), to_dev(c.v_cache)
+    bt = to_dev(c.block_tables)
+    kh, vh = c.k_cache, c.v_cache
+    for s, ch in enumerate(c.chunks):
+        pos = np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64)
+        seq = np.full(ch.q_len, s, dtype=np.int32)
+        pa.kv_write_fused(k, v, to_dev(ch.k_new), to_dev(ch.v_new), to_dev(pos), bt, to_dev(seq))
+        kh, vh = oracle.kv_write(kh, vh, ch.k_new, ch.v_new,
+                                 oracle.slot_mapping(pos, None, c.block_tables[s], B))
+    cu = np.array([0, 200, 210, 310], dtype=np.int32)
+    used = np.array([500, 5, 950], dtype=np.int32)       # B: 5 keys < 10 rows; C: 950 > 800
+    q = np.concatenate([ch.q for ch in c.chunks])
+    out = torch.full((310, 24, 256), 0x7FC0, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    log(f"{c.name} used={used.tolist()} max_seqlen_k=800")
+    pa.prefill_varlen(to_dev(q), k, v, bt, to_dev(cu), to_dev(used), 200, 800, c.scale,
+                      causal=True, out=out)
+    _sync()
+    got = bits(out)
+    assert np.all(got[200:210] == 0x7FC0), "rows of a sequence with fewer keys than rows were written"
+    ref_a = oracle.prefill_chunk(c.chunks[0].q, 300, True, kh, vh, c.block_tables[0], B, c.scale)
+    ref_c = oracle.prefill_chunk(c.chunks[2].q, 700, True, kh, vh, c.block_tables[2], B, c.scale)
+    compare(got[:200], ref_a, c.name + " A")
+    compare(got[210:], ref_c, c.name + " C (clamped)")
