@@ -5,7 +5,12 @@ with a version that carries one typical slip: a dropped scale, a wrong
 query-to-KV-head map, an off-by-one causal bound, swapped K and V, a block
 table that is not consulted, a wrong page offset, a decode that drops the
 newest key, a slot formula with page and offset swapped, a KV write one row
-off.  The pins of ``test_oracle_pins.py`` must fail for every one.
+off.  The pins of ``test_oracle_pins.py`` must fail for every one.  Further
+slips are planted in the single-token input prep (seq_lens without the +1, a
+running query_start_loc, the next page's slot, M-RoPE on one row only, the
+position as the token id) and in the page-size derivation (floor for ceiling,
+no rounding to the alignment, one group too many on an exact fit, only K's
+bytes per token).
 """
 import numpy as np
 import pytest
@@ -166,3 +171,47 @@ def test_input_prep_pins_catch_mutant(name, monkeypatch):
         except (AssertionError, ValueError, IndexError):
             caught += 1
     assert caught >= 1, f"mutant {name} passed every pin"
+
+
+# ---- page-size derivation ----------------------------------------------------
+
+def _page_floor(m, per_tok, align):
+    return (m // (align * per_tok)) * align
+
+
+def _page_no_alignment(m, per_tok, align):
+    return -(-m // per_tok)
+
+
+def _page_always_one_more(m, per_tok, align):
+    return (m // (align * per_tok) + 1) * align
+
+
+def _page_k_bytes_only(m, per_tok, align):
+    return -(-m // (align * (per_tok // 2))) * align
+
+
+PAGE_MUTANTS = {
+    "floor_not_ceil": _page_floor,
+    "no_alignment": _page_no_alignment,
+    "always_one_more_group": _page_always_one_more,
+    "k_bytes_only": _page_k_bytes_only,
+}
+PAGE_PINS = [pins.test_page_derivation_reproduces_printed_pages, pins.test_page_derivation_brute_force]
+
+
+@pytest.mark.parametrize("name", sorted(PAGE_MUTANTS))
+def test_page_pins_catch_mutant(name, monkeypatch):
+    monkeypatch.setattr(oracle, "required_page_tokens", PAGE_MUTANTS[name])
+    caught = 0
+    for call in PAGE_PINS:
+        try:
+            call()
+        except (AssertionError, ValueError, IndexError, ZeroDivisionError):
+            caught += 1
+    assert caught >= 1, f"mutant {name} passed every pin"
+
+
+def test_page_mutant_harness_passes_unmutated():
+    for call in PAGE_PINS:
+        call()
