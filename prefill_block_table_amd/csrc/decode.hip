@@ -676,10 +676,13 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   // covers every partial.  The partials of item i sit at slots
   // i + first .. i + first + nparts - 1, where (first, nparts) come from the
   // split kernel's meta; first is 0 for the batch's first item (every item of
-  // a single-sequence batch with <= 4 KV heads), so those loads are issued
-  // together with the meta load, assuming first = 0, and re-issued only when
-  // meta says otherwise.  Every slot below items + num_wgs is allocated, so
-  // the guessed loads stay in bounds.
+  // a single-sequence batch with <= 4 KV heads), so for one sequence those
+  // loads are issued together with the meta load, assuming first = 0, and
+  // re-issued only when meta says otherwise.  Every slot below items +
+  // num_wgs is allocated, so the guessed loads stay in bounds.  With several
+  // sequences most items have a single partial (the split kernel wrote their
+  // output) and the grid holds a workgroup per sequence: meta is read first,
+  // so those workgroups leave without touching the partials.
   constexpr int kParts = kMergeParts;
   const int64_t pml = (int64_t)hpw * (kGqa * 2);          // stride between consecutive slots
   const int64_t pacc = (int64_t)hpw * (kGqa * kHeadDim);
@@ -696,7 +699,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
       av[k] = ok ? *reinterpret_cast<const u32x2*>(acc + p * pacc) : u32x2{0u, 0u};
     }
   };
-  load_parts(item, a.num_wgs);
+  const bool guess = a.num_seqs == 1;
+  if (guess) load_parts(item, a.num_wgs);
   // meta of an empty sequence is stale and unused
   const int first = a.meta[2 * item];
   const int nparts = a.meta[2 * item + 1];
@@ -706,7 +710,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
     return;
   }
   if (nparts <= 1) return;                 // the split kernel wrote the output
-  if (first != 0) load_parts((int64_t)item + first, nparts);
+  if (!guess || first != 0) load_parts((int64_t)item + first, nparts);
 #pragma unroll
   for (int k = 0; k < kParts; ++k) {
     if (z + k * kMergeSlices >= nparts) { mlv[k] = f32x2{-INFINITY, 0.f}; av[k] = u32x2{0u, 0u}; }
