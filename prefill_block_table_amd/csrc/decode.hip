@@ -646,31 +646,43 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
 // z + kMergeSlices, ...; it reads dims 4*(t % (kMergeDims / 4)) .. +3 of the
 // slice, so with 32 dims eight threads read one partial slice (64 bytes of bf16).
 // (Measured: 32 dims per workgroup beats 16 and 8.)
+template <bool LOOP>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float red_o[4][kMergeDims];
   __shared__ float red_m[4];
   __shared__ float red_l[4];
-  // Workgroups go round-robin to the 8 XCDs (id % 8) and each XCD has its own
-  // L2, so the kLineSlices slices that share a 128-byte line of a partial
-  // are given ids with the same id % 8: each line is then fetched by one L2.
-  // gridDim.x = Hq * kHeadDim / kMergeDims is a multiple of 8 * kLineSlices.
-  const int xcd = blockIdx.x % 8;
-  const int q8 = blockIdx.x / 8;
-  const int slice = (q8 / kLineSlices * 8 + xcd) * kLineSlices + q8 % kLineSlices;
-  const int h = slice / (kHeadDim / kMergeDims);
-  const int dc = slice % (kHeadDim / kMergeDims);
+  // Slices dc0 .. dc0 + kNdc - 1 of query head h.  With LOOP (batches
+  // whose items outnumber the split workgroups, so most items have one or
+  // two partials) a workgroup takes every slice of (h, sequence) in turn: 8x
+  // fewer workgroups, most of which only read the item's meta and leave.
+  // Otherwise one workgroup per slice; workgroups go round-robin to the 8
+  // XCDs (id % 8) and each XCD has its own L2, so the kLineSlices slices that
+  // share a 128-byte line of a partial are given ids with the same id % 8:
+  // each line is then fetched by one L2.  gridDim.x = Hq * kHeadDim /
+  // kMergeDims is then a multiple of 8 * kLineSlices.
+  constexpr int kNdc = LOOP ? kHeadDim / kMergeDims : 1;
+  int h, dc0;
+  if constexpr (LOOP) {
+    h = blockIdx.x;
+    dc0 = 0;
+  } else {
+    const int xcd = blockIdx.x % 8;
+    const int q8 = blockIdx.x / 8;
+    const int slice = (q8 / kLineSlices * 8 + xcd) * kLineSlices + q8 % kLineSlices;
+    h = slice / (kHeadDim / kMergeDims);
+    dc0 = slice % (kHeadDim / kMergeDims);
+  }
   const int s = blockIdx.y;
   const int tid = threadIdx.x;
   const int z = tid / (kMergeDims / 4);
   const int dg = tid % (kMergeDims / 4);
-  const int d = dc * kMergeDims + 4 * dg;
   const int Hkv = a.num_kv_heads;
   const int hpw = a.heads_per_wg;
   const int g = h / kGqa;
   const int hh = h % kGqa;
   const int item = s * (Hkv / hpw) + g / hpw;
   const int jw = g % hpw;
-  uint16_t* outp = a.out + ((int64_t)s * Hkv * kGqa + h) * kHeadDim + d;
+  uint16_t* outh = a.out + ((int64_t)s * Hkv * kGqa + h) * kHeadDim + 4 * dg;
   // A workgroup leaves at most one partial per item and there are at most
   // kDecodeWorkgroups of them, so one round of kMergeParts loads per thread
   // covers every partial.  The partials of item i sit at slots
@@ -688,7 +700,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   const int64_t pacc = (int64_t)hpw * (kGqa * kHeadDim);
   f32x2 mlv[kParts];
   u32x2 av[kParts];
-  auto load_parts = [&](int64_t slot0, int count) {
+  auto load_parts = [&](int64_t slot0, int count, int d) {
     const float* ml = a.p_ml + (slot0 * hpw + jw) * (kGqa * 2) + 2 * hh;
     const uint16_t* acc = a.p_acc + (slot0 * hpw + jw) * (kGqa * kHeadDim) + hh * kHeadDim + d;
 #pragma unroll
@@ -699,18 +711,23 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
       av[k] = ok ? *reinterpret_cast<const u32x2*>(acc + p * pacc) : u32x2{0u, 0u};
     }
   };
-  const bool guess = a.num_seqs == 1;
-  if (guess) load_parts(item, a.num_wgs);
+  const bool guess = !LOOP && a.num_seqs == 1;   // LOOP runs with >= 16 sequences
+  if (guess) load_parts(item, a.num_wgs, dc0 * kMergeDims + 4 * dg);
   // meta of an empty sequence is stale and unused
   const int first = a.meta[2 * item];
   const int nparts = a.meta[2 * item + 1];
   const int L = clamp_len(a.seq_lens[s], a.max_seq_len);
   if (L == 0) {
-    if (z == 0) *reinterpret_cast<u32x2*>(outp) = u32x2{0u, 0u};
+    if (z == 0)
+      for (int i = 0; i < kNdc; ++i) *reinterpret_cast<u32x2*>(outh + (dc0 + i) * kMergeDims) = u32x2{0u, 0u};
     return;
   }
   if (nparts <= 1) return;                 // the split kernel wrote the output
-  if (!guess || first != 0) load_parts((int64_t)item + first, nparts);
+#pragma unroll 1
+  for (int i = 0; i < kNdc; ++i) {
+  const int dc = dc0 + i;
+  uint16_t* outp = outh + dc * kMergeDims;
+  if (!guess || first != 0 || dc != dc0) load_parts((int64_t)item + first, nparts, dc * kMergeDims + 4 * dg);
 #pragma unroll
   for (int k = 0; k < kParts; ++k) {
     if (z + k * kMergeSlices >= nparts) { mlv[k] = f32x2{-INFINITY, 0.f}; av[k] = u32x2{0u, 0u}; }
@@ -759,6 +776,8 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
     const float inv = 1.f / Ls;
     *reinterpret_cast<u32x2*>(outp) = u32x2{pack_bf16x2(O[0] * inv, O[1] * inv),
                                              pack_bf16x2(O[2] * inv, O[3] * inv)};
+  }
+  if (i + 1 < kNdc) __syncthreads();   // red_o is rewritten by the next slice
   }
 }
 
@@ -841,8 +860,14 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(decode_merge_kernel, dim3(num_kv_heads * kGqa * (kHeadDim / kMergeDims), num_seqs),
-                     dim3(256), 0, stream, a);
+  // Items at least as many as split workgroups: an item of average length
+  // spans at most two workgroups, so most items need no merge, and one merge
+  // workgroup per (head, sequence) takes all of its slices.
+  if ((int64_t)num_seqs * (num_kv_heads / plan.heads_per_wg) >= plan.num_wgs)
+    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(num_kv_heads * kGqa, num_seqs), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(num_kv_heads * kGqa * (kHeadDim / kMergeDims), num_seqs),
+                       dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -282,6 +282,21 @@ def test_more_than_256_sequences(append):
         compare(run_gpu(c), run_oracle(c), c.name)
 
 
+def test_many_sequences_with_long_ones():
+    """300 sequences, most short, three of 12K-20K tokens: with more items
+    than split workgroups the merge takes one workgroup per (head, sequence)
+    over every slice, and the long items there combine dozens of partials."""
+    rng = np.random.Generator(np.random.PCG64(79))
+    lens = [int(x) for x in rng.integers(1, 400, size=300)]
+    for j, n in ((5, 12000), (150, 20000), (299, 16001)):
+        lens[j] = n
+    B = 64
+    pages = sum(-(-(n + 1) // B) for n in lens) + 3
+    c = W.make_decode_case("seqs300_long", 80, lens, B, pages, write_new_token=True)
+    log(c.name)
+    _check_append(c)
+
+
 RANDOM_CASES = 16
 
 
