@@ -646,26 +646,18 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
 // z + kMergeSlices, ...; it reads dims 4*(t % (kMergeDims / 4)) .. +3 of the
 // slice, so with 32 dims eight threads read one partial slice (64 bytes of bf16).
 // (Measured: 32 dims per workgroup beats 16 and 8.)
-template <bool LOOP>
 __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(16))) float red_o[4][kMergeDims];
   __shared__ float red_m[4];
   __shared__ float red_l[4];
-  // Slices dc0 .. dc0 + kNdc - 1 of query head h.  With LOOP (batches
-  // whose items outnumber the split workgroups, so most items have one or
-  // two partials) a workgroup takes every slice of (h, sequence) in turn: 8x
-  // fewer workgroups, most of which only read the item's meta and leave.
-  // Otherwise one workgroup per slice; workgroups go round-robin to the 8
-  // XCDs (id % 8) and each XCD has its own L2, so the kLineSlices slices that
-  // share a 128-byte line of a partial are given ids with the same id % 8:
-  // each line is then fetched by one L2.  gridDim.x = Hq * kHeadDim /
-  // kMergeDims is then a multiple of 8 * kLineSlices.
-  constexpr int kNdc = LOOP ? kHeadDim / kMergeDims : 1;
+  // One workgroup per slice dc0 of query head h (kNdc = 1 slice each).
+  // Workgroups go round-robin to the 8 XCDs (id % 8) and each XCD has its own
+  // L2, so the kLineSlices slices that share a 128-byte line of a partial are
+  // given ids with the same id % 8: each line is then fetched by one L2.
+  // gridDim.x = Hq * kHeadDim / kMergeDims is a multiple of 8 * kLineSlices.
+  constexpr int kNdc = 1;
   int h, dc0;
-  if constexpr (LOOP) {
-    h = blockIdx.x;
-    dc0 = 0;
-  } else {
+  {
     const int xcd = blockIdx.x % 8;
     const int q8 = blockIdx.x / 8;
     const int slice = (q8 / kLineSlices * 8 + xcd) * kLineSlices + q8 % kLineSlices;
@@ -691,10 +683,9 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
   // a single-sequence batch with <= 4 KV heads), so for one sequence those
   // loads are issued together with the meta load, assuming first = 0, and
   // re-issued only when meta says otherwise.  Every slot below items +
-  // num_wgs is allocated, so the guessed loads stay in bounds.  With several
-  // sequences most items have a single partial (the split kernel wrote their
-  // output) and the grid holds a workgroup per sequence: meta is read first,
-  // so those workgroups leave without touching the partials.
+  // num_wgs is allocated, so the guessed loads stay in bounds.  (Batches of
+  // several sequences go to decode_merge_wide_kernel; should one come here,
+  // meta is read first.)
   constexpr int kParts = kMergeParts;
   const int64_t pml = (int64_t)hpw * (kGqa * 2);          // stride between consecutive slots
   const int64_t pacc = (int64_t)hpw * (kGqa * kHeadDim);
@@ -711,7 +702,7 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
       av[k] = ok ? *reinterpret_cast<const u32x2*>(acc + p * pacc) : u32x2{0u, 0u};
     }
   };
-  const bool guess = !LOOP && a.num_seqs == 1;   // LOOP runs with >= 16 sequences
+  const bool guess = a.num_seqs == 1;
   if (guess) load_parts(item, a.num_wgs, dc0 * kMergeDims + 4 * dg);
   // meta of an empty sequence is stale and unused
   const int first = a.meta[2 * item];
@@ -778,6 +769,95 @@ __global__ void __launch_bounds__(256) decode_merge_kernel(DecodeArgs a) {
                                              pack_bf16x2(O[2] * inv, O[3] * inv)};
   }
   if (i + 1 < kNdc) __syncthreads();   // red_o is rewritten by the next slice
+  }
+}
+
+// Merge for batches of several sequences: one workgroup per (query head,
+// sequence) covers all 256 dims at once (lane l: dims 4l .. 4l+3), and wave w
+// takes partials w, w + 4, ... of the item, four at a time, with an online
+// re-basing of its running max.  Most items of a batch have one partial (the
+// split kernel wrote their output) or a few, so a workgroup reads the item's
+// meta and then needs at most one round of loads per wave; the per-slice
+// kernel would give each of those items 8 workgroups with a round trip each.
+// The four waves combine through LDS in a fixed order (bitwise repeatable).
+__global__ void __launch_bounds__(256) decode_merge_wide_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(16))) float red_o[4][kHeadDim];
+  __shared__ float red_m[4];
+  __shared__ float red_l[4];
+  const int h = blockIdx.x;
+  const int s = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int Hkv = a.num_kv_heads;
+  const int hpw = a.heads_per_wg;
+  const int g = h / kGqa;
+  const int hh = h % kGqa;
+  const int item = s * (Hkv / hpw) + g / hpw;
+  const int jw = g % hpw;
+  const int d = 4 * lane;
+  uint16_t* outp = a.out + ((int64_t)s * Hkv * kGqa + h) * kHeadDim + d;
+  // meta of an empty sequence is stale and unused
+  const int first = a.meta[2 * item];
+  const int nparts = a.meta[2 * item + 1];
+  const int L = clamp_len(a.seq_lens[s], a.max_seq_len);
+  if (L == 0) {
+    if (w == 0) *reinterpret_cast<u32x2*>(outp) = u32x2{0u, 0u};
+    return;
+  }
+  if (nparts <= 1) return;                 // the split kernel wrote the output
+  const int64_t slot0 = (int64_t)item + first;
+  const int64_t pml = (int64_t)hpw * (kGqa * 2);          // stride between consecutive slots
+  const int64_t pacc = (int64_t)hpw * (kGqa * kHeadDim);
+  const float* ml = a.p_ml + (slot0 * hpw + jw) * (kGqa * 2) + 2 * hh;
+  const uint16_t* acc = a.p_acc + (slot0 * hpw + jw) * (kGqa * kHeadDim) + hh * kHeadDim + d;
+  float M = -INFINITY;
+  float Ls = 0.f;
+  f32x4 O = {0.f, 0.f, 0.f, 0.f};
+  for (int p0 = w; p0 < nparts; p0 += 16) {
+    f32x2 mlv[4];
+    u32x2 av[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int p = p0 + 4 * k;
+      const bool ok = p < nparts;
+      mlv[k] = ok ? *reinterpret_cast<const f32x2*>(ml + p * pml) : f32x2{-INFINITY, 0.f};
+      av[k] = ok ? *reinterpret_cast<const u32x2*>(acc + p * pacc) : u32x2{0u, 0u};
+    }
+    float Mn = M;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Mn = fmaxf(Mn, mlv[k][0]);
+    const float base = Mn == -INFINITY ? 0.f : Mn;
+    const float c = fast_exp2(M - base);   // 0 while nothing was added
+    Ls *= c;
+    O *= c;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float f = fast_exp2(mlv[k][0] - base) * mlv[k][1];
+      Ls += f;
+      O += f * f32x4{bf16_lo(av[k][0]), bf16_hi(av[k][0]), bf16_lo(av[k][1]), bf16_hi(av[k][1])};
+    }
+    M = Mn;
+  }
+  *reinterpret_cast<f32x4*>(&red_o[w][d]) = O;
+  if (lane == 0) { red_m[w] = M; red_l[w] = Ls; }
+  __syncthreads();
+  if (w == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) Mt = fmaxf(Mt, red_m[ww]);
+    const float mt = Mt == -INFINITY ? 0.f : Mt;
+    float Lt = 0.f;
+    f32x4 Ot = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = fast_exp2(red_m[ww] - mt);
+      Lt += f * red_l[ww];
+      Ot += f * *reinterpret_cast<const f32x4*>(&red_o[ww][d]);
+    }
+    const float inv = 1.f / Lt;
+    *reinterpret_cast<u32x2*>(outp) = u32x2{pack_bf16x2(Ot[0] * inv, Ot[1] * inv),
+                                             pack_bf16x2(Ot[2] * inv, Ot[3] * inv)};
   }
 }
 
@@ -860,14 +940,11 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // Items at least as many as split workgroups: an item of average length
-  // spans at most two workgroups, so most items need no merge, and one merge
-  // workgroup per (head, sequence) takes all of its slices.
-  if ((int64_t)num_seqs * (num_kv_heads / plan.heads_per_wg) >= plan.num_wgs)
-    hipLaunchKernelGGL(decode_merge_kernel<true>, dim3(num_kv_heads * kGqa, num_seqs), dim3(256), 0, stream, a);
+  if (num_seqs == 1)
+    hipLaunchKernelGGL(decode_merge_kernel, dim3(num_kv_heads * kGqa * (kHeadDim / kMergeDims)), dim3(256), 0,
+                       stream, a);
   else
-    hipLaunchKernelGGL(decode_merge_kernel<false>, dim3(num_kv_heads * kGqa * (kHeadDim / kMergeDims), num_seqs),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(decode_merge_wide_kernel, dim3(num_kv_heads * kGqa, num_seqs), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
