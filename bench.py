@@ -54,6 +54,53 @@ def kv_bytes(seq_lens, num_kv_heads=4):
     return int(sum(int(x) for x in seq_lens)) * num_kv_heads * 256 * 2 * 2
 
 
+SERVING_BATCHES = ((512, 256), (256, 1024), (128, 512), (64, 2048))
+
+
+def bench_decode_serving(D, pa, steps=100, warmup=10, block_size=64):
+    """Serving-style decode batches: S sequences of L cached tokens each plus
+    the appended one, 24 / 4 heads, page 64, random page placement; the
+    caches are drawn on the device (seeded) and rotated over >= 2 GiB of
+    replicas as in the other decode legs.  Returns per-batch timings."""
+    torch = D.torch
+    res = {}
+    for S, L in SERVING_BATCHES:
+        g = torch.Generator(device=D.dev).manual_seed(1000 * S + L)
+        per = -(-(L + 1) // block_size)
+        P = S * per + 1
+        k0 = torch.randn(P, block_size, 4, 256, device=D.dev, generator=g).to(torch.bfloat16)
+        v0 = torch.randn(P, block_size, 4, 256, device=D.dev, generator=g).to(torch.bfloat16)
+        reps = max(1, math.ceil(MALL_DEFEAT_BYTES / (2 * k0.numel() * 2)))
+        ks, vs = [k0], [v0]
+        for _ in range(reps - 1):
+            ks.append(k0.clone())
+            vs.append(v0.clone())
+        bt = torch.randperm(P - 1, device=D.dev, generator=g)[: S * per].view(S, per).to(torch.int32)
+        sl = torch.full((S,), L + 1, dtype=torch.int32, device=D.dev)
+        q = torch.randn(S, 24, 256, device=D.dev, generator=g).to(torch.bfloat16)
+        kn = torch.randn(S, 4, 256, device=D.dev, generator=g).to(torch.bfloat16)
+        vn = torch.randn(S, 4, 256, device=D.dev, generator=g).to(torch.bfloat16)
+        ws = pa.decode_workspace(S, L + 1, block_size, device=D.dev)
+        out = torch.empty_like(q)
+        for i in range(warmup):
+            pa.decode_append(q, ks[i % reps], vs[i % reps], bt, sl, L + 1, 0.0625, kn, vn, workspace=ws, out=out)
+        torch.cuda.synchronize()
+        torch.cuda._sleep(int(50e6))               # let the host enqueue ahead of the device
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(steps):
+            pa.decode_append(q, ks[i % reps], vs[i % reps], bt, sl, L + 1, 0.0625, kn, vn, workspace=ws, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        nbytes = S * (L + 1) * 4 * 256 * 2 * 2
+        res[f"{S}x{L}"] = {"ms_per_step": ms, "kv_bytes": nbytes, "gbs": nbytes / (ms * 1e-3) / 1e9,
+                           "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, "replicas": reps}
+        del ks, vs, k0, v0
+        torch.cuda.empty_cache()
+    return res
+
+
 def causal_flops(start, q_len, num_q_heads=24, head_dim=256):
     pairs = q_len * start + q_len * (q_len + 1) // 2
     return 4 * head_dim * num_q_heads * pairs
@@ -511,6 +558,8 @@ def main():
         extra["decode_batch16_ctx4k_32k_b832"] = bench_decode(D, pa, W.batched_decode(),
                                                               max(20, args.steps // 4),
                                                               args.warmup, rotate=True)
+        print("[bench] decode serving batches", file=sys.stderr, flush=True)
+        extra["decode_serving_b64"] = bench_decode_serving(D, pa)
         print("[bench] decode input prep", file=sys.stderr, flush=True)
         extra["decode_input_prep"] = bench_input_prep(D, pa)
         print("[bench] gemv", file=sys.stderr, flush=True)
