@@ -29,7 +29,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor spec
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_ctx8192_b832_hbm_traffic.json")
 DECODE_SRC = os.path.join(ROOT, "prefill_block_table_amd", "csrc", "decode.hip")
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor spec
-MALL_DEFEAT_BYTES = 2 << 30    # rotate pool replicas over at least this many bytes
+MALL_DEFEAT_BYTES = 2 << 30    # rotate pool replicas so that the K/V bytes the steps
+                               # touch cycle over at least this many bytes (8x the
+                               # 256 MB Infinity Cache)
 
 
 def parse():
@@ -170,8 +172,10 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=N
     followed by a decode call."""
     torch = D.torch
     k0, v0 = D.t(case.k_cache), D.t(case.v_cache)
-    pool_bytes = 2 * k0.numel() * 2
-    reps = max(1, math.ceil(MALL_DEFEAT_BYTES / pool_bytes)) if rotate else 1
+    # replicas sized by the bytes a step touches (not the pool's size), so
+    # the rotation cycles over >= MALL_DEFEAT_BYTES of K/V that steps read
+    touched = kv_bytes(case.seq_lens)
+    reps = max(2, math.ceil(MALL_DEFEAT_BYTES / touched)) if rotate else 1
     ks, vs = [k0], [v0]
     for _ in range(reps - 1):
         ks.append(k0.clone())
@@ -198,7 +202,7 @@ def bench_decode(D, pa, case, steps, warmup, rotate=True, graph=False, hold_ms=N
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    res = {"replicas": reps}
+    res = {"replicas": reps, "rotated_kv_bytes": reps * touched if rotate else touched}
     nbytes = kv_bytes(case.seq_lens)
     if graph:
         # one graph holds one step per replica; replayed until >= steps steps ran
@@ -288,6 +292,68 @@ def bench_prefill(D, pa, case, steps, warmup):
             frac_bf16_peak=fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             kv_write_ms=w0.elapsed_time(w1), kv_write_bytes=ch.q_len * 4 * 256 * 2 * 2)
     return out
+
+
+VARLEN_SEED = 808
+
+
+def varlen_batch():
+    """8 sequences, each one chunk of 256-4096 query rows at a start position in
+    [0, 8192] (seeded), page 832: a batched chunked-prefill step."""
+    import numpy as np
+    rng = np.random.Generator(np.random.PCG64(VARLEN_SEED))
+    q_lens = rng.integers(256, 4096, size=8, endpoint=True)
+    starts = rng.integers(0, 8192, size=8, endpoint=True)
+    return [(int(s0), int(n)) for s0, n in zip(starts, q_lens)]
+
+
+def bench_prefill_varlen(D, pa, W, steps, warmup, block_size=832):
+    """pa_prefill_varlen on the 8-sequence batch above: every sequence's chunk
+    K/V written first, then back-to-back launches; TFLOP/s over the causal
+    flops of all sequences."""
+    torch = D.torch
+    np = D.np
+    seqs = varlen_batch()
+    pages = sum(-(-(s0 + n) // block_size) for s0, n in seqs)
+    c = W.make_varlen_prefill_case("varlen8", VARLEN_SEED, seqs, block_size, pages + 4)
+    k, v = D.t(c.k_cache), D.t(c.v_cache)
+    bt = D.t(c.block_tables)
+    for s, ch in enumerate(c.chunks):
+        pos = D.t(np.arange(ch.start_pos, ch.start_pos + ch.q_len, dtype=np.int64))
+        seq = D.t(np.full(ch.q_len, s, dtype=np.int32))
+        pa.kv_write_fused(k, v, D.t(ch.k_new), D.t(ch.v_new), pos, bt, seq)
+    lens = [ch.q_len for ch in c.chunks]
+    cu = D.t(np.concatenate([[0], np.cumsum(lens)]).astype(np.int32))
+    used_np = np.array([ch.start_pos + ch.q_len for ch in c.chunks], dtype=np.int32)
+    used = D.t(used_np)
+    q = D.t(np.concatenate([ch.q for ch in c.chunks]))
+    o = torch.empty_like(q)
+    ws = pa.prefill_varlen_workspace(cu, used, max(lens), int(used_np.max()), block_size,
+                                     device=D.dev) if hasattr(pa, "prefill_varlen_workspace") else None
+
+    def step(i, ev):
+        if ev is not None:
+            ev[0].record()
+        if ws is None:
+            pa.prefill_varlen(q, k, v, bt, cu, used, max(lens), int(used_np.max()), c.scale,
+                              causal=True, out=o)
+        else:
+            pa.prefill_varlen(q, k, v, bt, cu, used, max(lens), int(used_np.max()), c.scale,
+                              causal=True, out=o, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(warmup):
+        step(i, None)
+    hold = 2.0 * steps + 5.0
+    total_ms, _, _ = timed_loop(torch, steps, step, hold, events=False)
+    _, kern, _ = timed_loop(torch, steps, step, hold)
+    avg = total_ms / steps
+    fl = sum(causal_flops(s0, n) for s0, n in seqs)
+    return dict(_stats(kern), seqs=[{"start": s0, "q_len": n} for s0, n in seqs],
+                block_size=block_size, ms_per_launch=avg, causal_flops=fl,
+                tflops=fl / (avg * 1e-3) / 1e12,
+                frac_bf16_peak=fl / (avg * 1e-3) / 1e12 / BF16_PEAK_TFLOPS)
 
 
 def bench_input_prep(D, pa, iters=2000, warmup=100):
@@ -567,6 +633,21 @@ def main():
         print("[bench] prefill", file=sys.stderr, flush=True)
         extra["prefill_b832"] = bench_prefill(D, pa, W.prefill_8k(), max(10, args.steps // 5),
                                               min(args.warmup, 5))
+        for B in (784, 1024):
+            # the same chunks on the other page sizes (same causal flops)
+            print(f"[bench] prefill page {B}", file=sys.stderr, flush=True)
+            extra[f"prefill_b{B}"] = bench_prefill(
+                D, pa, W.make_prefill_case(f"prefill_q4096_s4096_then_q1685_b{B}", 3,
+                                           [(4096, 4096), (8192, 1685)], B, 128),
+                max(10, args.steps // 5), min(args.warmup, 5))
+        for key in ("q4096_start4096", "q1685_start8192"):
+            base = extra["prefill_b832"][key]["ms_per_launch"]
+            for B in (784, 1024):
+                extra[f"prefill_b{B}"][key]["ratio_to_b832"] = round(
+                    extra[f"prefill_b{B}"][key]["ms_per_launch"] / base, 4)
+        print("[bench] prefill varlen", file=sys.stderr, flush=True)
+        extra["prefill_varlen8_b832"] = bench_prefill_varlen(D, pa, W, max(10, args.steps // 5),
+                                                             min(args.warmup, 5))
     torch.cuda.synchronize()
 
     cpu = None

@@ -33,8 +33,11 @@
  *    block_table[logical_page]).
  *  - Supported shapes: head_dim == 256, num_q_heads == 6 * num_kv_heads
  *    (GQA ratio 6, [ALIGN] §4), 1 <= num_kv_heads <= 64.  Others return
- *    PA_ERR_UNSUPPORTED.  Any block_size >= 1 works; pages whose size is not
- *    a multiple of 64 cost one masked tail group per page.
+ *    PA_ERR_UNSUPPORTED.  Any block_size >= 1 works as long as one page of
+ *    one cache, block_size * num_kv_heads * 256 * 2 bytes, stays below
+ *    4 GiB (kernels address rows inside a page with 32-bit byte offsets;
+ *    larger pages return PA_ERR_BLOCK_SIZE); pages whose size is not a
+ *    multiple of 64 cost one masked tail group per page.
  *  - Ownership: the caller owns every buffer, including the decode
  *    workspace.  The library never allocates or frees device memory and
  *    keeps no state between calls.
@@ -60,7 +63,7 @@ extern "C" {
 
 #define PA_OK 0
 #define PA_ERR_NULL -1          /* a required pointer is NULL */
-#define PA_ERR_BLOCK_SIZE -2    /* block_size < 1 */
+#define PA_ERR_BLOCK_SIZE -2    /* block_size < 1, or one page of one cache >= 4 GiB */
 #define PA_ERR_UNSUPPORTED -3   /* head_dim / head counts outside the supported set */
 #define PA_ERR_SIZE -4          /* a count or position is out of range */
 #define PA_ERR_WORKSPACE -5     /* decode workspace NULL or too small */
@@ -174,11 +177,17 @@ int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
  * k_cache, v_cache  modified in place: row pos % block_size of page
  *                   block_table[s][pos / block_size] receives k_new[s] /
  *                   v_new[s].  That page must be a valid page (it is read
- *                   by the decode as well); sequences of length 0 write
- *                   nothing.
+ *                   by the decode as well); sequences of length <= 0 write
+ *                   nothing.  A sequence with seq_lens[s] > max_seq_len
+ *                   attends its first max_seq_len cached keys unchanged
+ *                   (as pa_decode does) and its new token is stored at
+ *                   pos = seq_lens[s] - 1 when pos / block_size < bt_stride
+ *                   (that entry must then be a valid page), otherwise not
+ *                   stored (slot -1), exactly as the fused write above.
  * k_new, v_new      bf16 [num_seqs][num_kv_heads][256], 16-byte aligned.
  * slot_out          int64 [num_seqs] or NULL: the slot of each appended
- *                   token (not written for sequences of length 0).
+ *                   token (-1 when its logical page is past the table row;
+ *                   not written for sequences of length <= 0).
  * Other arguments, the workspace and errors: as pa_decode.
  */
 int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16_t* v_cache,

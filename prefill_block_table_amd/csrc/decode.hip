@@ -213,9 +213,10 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
   int s_cur = 0;
   int seq_start = 0;    // flattened index of the first step of s_cur
   const bool single = a.num_seqs == 1;
-  int L_single = 0;
+  int L_single = 0, raw_single = 0;
   if (single) {
-    L_single = clamp_len(load_const_i32(a.seq_lens), a.max_seq_len);
+    raw_single = load_const_i32(a.seq_lens);
+    L_single = clamp_len(raw_single, a.max_seq_len);
     T = live_steps(L_single, B, spp, STOK) * ng;
   } else {
     for (int c0 = 0; c0 < a.num_seqs; c0 += 256) {
@@ -355,8 +356,14 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
     // Appending (pa_decode_append): the step holding the new token takes its
     // K/V rows straight from k_new / v_new (see issue); the workgroup that
     // owns the item's last step also stores them to the cache (after its
-    // loop).  Nothing else in the launch reads that cache row.
+    // loop).  Nothing else in the launch reads that cache row.  A sequence
+    // whose length is above max_seq_len attends its first max_seq_len cached
+    // rows as they are (no fresh row among them) and stores the new token at
+    // position seq_lens - 1, past every row the launch reads, as the
+    // separate slot-mapping write would.
     const bool append = a.k_new != nullptr;
+    const int raw = !append ? L : (single ? raw_single : __builtin_amdgcn_readfirstlane(load_const_i32(a.seq_lens + s)));
+    const bool fresh_ok = append && raw <= a.max_seq_len;
     const char* knew = append ? reinterpret_cast<const char*>(a.k_new + ((int64_t)s * Hkv + g) * kHeadDim) : nullptr;
     const char* vnew = append ? reinterpret_cast<const char*>(a.v_new + ((int64_t)s * Hkv + g) * kHeadDim) : nullptr;
     const bool append_store = append && lb == steps && ks == 0;
@@ -405,7 +412,7 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
       const int page_len = min(B, L - ip * B);      // live rows of the page
       // rows up to lim - 1 come from the cache as they are; the rest are
       // masked rows (or, when appending, the new token's row and after)
-      const int lim = (append && ip == last_page) ? page_len - 1 : page_len;
+      const int lim = (fresh_ok && ip == last_page) ? page_len - 1 : page_len;
       if (kb + 16 <= lim) {
         const char* kp = kcache + ip_base + (uint32_t)kb * rs_bytes + k_lane;
         const char* vp = vcache + ip_base + (uint32_t)kb * rs_bytes + v_lane_src;
@@ -419,7 +426,7 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
         // k_new / v_new.
         {
           const int key = kb + c16;
-          const bool fresh = key >= lim && append && ip == last_page;
+          const bool fresh = key >= lim && fresh_ok && ip == last_page;
           const char* kp = fresh ? knew + 16 * kq
                                  : kcache + ip_base + (uint32_t)(key < lim ? key : 0) * rs_bytes + 16 * kq;
 #pragma unroll
@@ -428,7 +435,7 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
 #pragma unroll
         for (int jj = 0; jj < 8; ++jj) {
           const int key = kb + 2 * jj + half;
-          const bool fresh = key >= lim && append && ip == last_page;
+          const bool fresh = key >= lim && fresh_ok && ip == last_page;
           const char* vp = fresh ? vnew + 16 * pos
                                  : vcache + ip_base + (uint32_t)(key < lim ? key : 0) * rs_bytes + 16 * pos;
           vreg[j][jj] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(vp));
@@ -560,12 +567,20 @@ __global__ void __launch_bounds__(256, 1) decode_split_kernel(DecodeArgs a) {
       if (i + kStages < nsteps) issue(j % kStages);
     }
     if (append_store) {
-      const int64_t page_id = load_const_i32(bt + last_page);
-      const int64_t off = (int64_t)(L - 1) - (int64_t)last_page * B;
-      const int64_t dst = page_id * a.page_stride + off * Hkv * kHeadDim + (int64_t)g * kHeadDim + 4 * lane;
-      *reinterpret_cast<u32x2*>(a.k_dst + dst) = knew_v;
-      *reinterpret_cast<u32x2*>(a.v_dst + dst) = vnew_v;
-      if (a.slot_out && jw == 0 && lane == 0) a.slot_out[s] = page_id * B + off;
+      // position of the new token and its logical page; a page past the
+      // table row gives slot -1 and no store (as the slot mapping defines)
+      const int64_t pos_new = (int64_t)(fresh_ok ? L : raw) - 1;
+      const int64_t lp = pos_new / B;
+      if (lp < a.bt_stride) {
+        const int64_t page_id = load_const_i32(bt + lp);
+        const int64_t off = pos_new - lp * B;
+        const int64_t dst = page_id * a.page_stride + off * Hkv * kHeadDim + (int64_t)g * kHeadDim + 4 * lane;
+        *reinterpret_cast<u32x2*>(a.k_dst + dst) = knew_v;
+        *reinterpret_cast<u32x2*>(a.v_dst + dst) = vnew_v;
+        if (a.slot_out && jw == 0 && lane == 0) a.slot_out[s] = page_id * B + off;
+      } else if (a.slot_out && jw == 0 && lane == 0) {
+        a.slot_out[s] = -1;
+      }
     }
     // Partial slots of this item: its workgroups are consecutive; only the
     // workgroup's first item can have started in an earlier workgroup and

@@ -34,6 +34,8 @@ int check_cache(const uint16_t* k_cache, const uint16_t* v_cache, int64_t page_s
                 int32_t block_size, int32_t num_kv_heads) {
   if (!k_cache || !v_cache) return PA_ERR_NULL;
   if (block_size < 1) return PA_ERR_BLOCK_SIZE;
+  // Kernels address rows inside a page with 32-bit byte offsets.
+  if ((int64_t)block_size * num_kv_heads * pa::kHeadDimAbi * 2 >= ((int64_t)1 << 32)) return PA_ERR_BLOCK_SIZE;
   if (page_stride < (int64_t)block_size * num_kv_heads * pa::kHeadDimAbi) return PA_ERR_STRIDE;
   if (page_stride % 8 != 0) return PA_ERR_ALIGN;
   if (!aligned16(k_cache) || !aligned16(v_cache)) return PA_ERR_ALIGN;
@@ -315,7 +317,7 @@ const char* pa_strerror(int code) {
   switch (code) {
     case PA_OK: return "ok";
     case PA_ERR_NULL: return "a required pointer is NULL";
-    case PA_ERR_BLOCK_SIZE: return "block_size must be >= 1";
+    case PA_ERR_BLOCK_SIZE: return "block_size must be >= 1 and one page of one cache below 4 GiB";
     case PA_ERR_UNSUPPORTED: return "unsupported shape: need head_dim 256, num_q_heads = 6 * num_kv_heads, 1 <= num_kv_heads <= 64";
     case PA_ERR_SIZE: return "a count or position is out of range";
     case PA_ERR_WORKSPACE: return "workspace is NULL or smaller than pa_decode_workspace_size() / pa_prefill_workspace_size()";

@@ -238,3 +238,21 @@ def test_gemv_validation():
     assert call(y=ctypes.c_void_p(0x10001)) == C["PA_ERR_ALIGN"]
     assert call(y=FAKE_MIS, f32=1) == C["PA_ERR_ALIGN"]
     assert call(N=0, y=None, W=None, x=None) == C["PA_OK"]   # nothing to do, nothing launched
+
+
+def test_pages_of_4gib_rejected():
+    """Rows inside a page are addressed with 32-bit byte offsets: a page of
+    one cache of 2^32 bytes or more (block_size * num_kv_heads * 512) is
+    rejected before anything is enqueued, by every call that takes a cache."""
+    big4 = 2 ** 21                       # 4 KV heads: 2^21 * 4 * 512 = 2^32 bytes
+    big64 = 2 ** 17                      # 64 KV heads: 2^17 * 64 * 512 = 2^32 bytes
+    assert _decode(B=big4, page_stride=big4 * 1024, bt_stride=1, max_seq_len=100) == C["PA_ERR_BLOCK_SIZE"]
+    assert _decode(B=big64, page_stride=big64 * 64 * 256, bt_stride=1, max_seq_len=100, hkv=64,
+                   hq=384) == C["PA_ERR_BLOCK_SIZE"]
+    assert _append(B=big4, page_stride=big4 * 1024, bt_stride=1, max_seq_len=100) == C["PA_ERR_BLOCK_SIZE"]
+    assert _prefill(B=big4, page_stride=big4 * 1024, n_bt=1) == C["PA_ERR_BLOCK_SIZE"]
+    assert pa.lib.pa_kv_write(FAKE, FAKE, big4 * 1024, 4, big4, 4, 256, FAKE, FAKE, 1, FAKE,
+                              None) == C["PA_ERR_BLOCK_SIZE"]
+    # one below the limit passes the page-size check (and fails on a later one)
+    assert _decode(B=big4 - 1, page_stride=big4 * 1024, bt_stride=1, max_seq_len=100,
+                   ws=None) == C["PA_ERR_WORKSPACE"]

@@ -335,3 +335,123 @@ def test_seq_lens_clamped_to_range():
     got = bits(out)
     assert np.all(got[0] == 0)
     compare(got[1:], ref[1:], c.name)
+
+
+@pytest.mark.parametrize("table_width", [47, 40])
+def test_append_seq_lens_above_max_matches_two_call_path(table_width):
+    """pa_decode_append with lengths outside [1, max_seq_len]: seq_lens
+    [-5, 3000, 700] at max_seq_len 2500 on page 64.  The sequence above the
+    bound attends its first 2500 cached keys unchanged and its new token goes
+    to position 2999 (logical page 46), as pa_kv_write_fused at position
+    seq_lens - 1 would put it: into the table's entry 46 when the row has 47
+    entries, nowhere (slot -1) when it has 40.  Cache bits, output bits and
+    the slots must equal the two-call path (kv_write_fused, then decode)."""
+    import torch
+    pa = _pa()
+    B = 64
+    c = W.make_decode_case(f"append_over_w{table_width}", 42, [1, 2500, 700], B, 4 + 40 + 11 + 3,
+                           write_new_token=False, table_width=table_width)
+    rng = np.random.Generator(np.random.PCG64(4242))
+    k_new = W.normal_bf16(rng, (3, 4, 256))
+    v_new = W.normal_bf16(rng, (3, 4, 256))
+    lens = np.array([-5, 3000, 700], dtype=np.int32)
+    bt = to_dev(c.block_tables)
+    log(f"{c.name} seq_lens={lens.tolist()} max_seq_len=2500 bt_stride={c.block_tables.shape[1]}")
+    # one launch
+    k1, v1 = to_dev(c.k_cache), to_dev(c.v_cache)
+    s1 = torch.full((3,), -7, dtype=torch.int64, device="cuda")
+    o1 = pa.decode_append(to_dev(c.q), k1, v1, bt, to_dev(lens), 2500, c.scale, to_dev(k_new),
+                          to_dev(v_new), slot_out=s1)
+    # two calls
+    k2, v2 = to_dev(c.k_cache), to_dev(c.v_cache)
+    s2 = torch.full((3,), -7, dtype=torch.int64, device="cuda")
+    pa.kv_write_fused(k2, v2, to_dev(k_new), to_dev(v_new), to_dev(lens.astype(np.int64) - 1), bt,
+                      to_dev(np.arange(3, dtype=np.int32)), slot_out=s2)
+    o2 = pa.decode(to_dev(c.q), k2, v2, bt, to_dev(lens), 2500, c.scale)
+    _sync()
+    assert np.array_equal(bits(k1), bits(k2)) and np.array_equal(bits(v1), bits(v2))
+    assert np.array_equal(bits(o1), bits(o2))
+    sl1, sl2 = s1.cpu().numpy(), s2.cpu().numpy()
+    assert sl1[0] == -7                              # length <= 0: slot not written
+    assert np.array_equal(sl1[1:], sl2[1:])
+    want = -1 if table_width <= 46 else int(c.block_tables[1, 46]) * B + 2999 % B
+    assert sl1[1] == want
+    # the written row, and the outputs against the oracle (first 2500 keys)
+    ref_slots = oracle.slot_mapping(np.array([2999, 699]), np.array([1, 2]), c.block_tables, B) \
+        if table_width > 46 else oracle.slot_mapping(np.array([699]), np.array([2]), c.block_tables, B)
+    kr, vr = oracle.kv_write(c.k_cache, c.v_cache, k_new[1:] if table_width > 46 else k_new[2:],
+                             v_new[1:] if table_width > 46 else v_new[2:], ref_slots)
+    assert np.array_equal(bits(k1), kr) and np.array_equal(bits(v1), vr)
+    got = bits(o1)
+    assert np.all(got[0] == 0)
+    ref = oracle.decode(c.q, kr, vr, c.block_tables, np.array([1, 2500, 700], np.int32), B, c.scale,
+                        seqs=[1, 2])
+    compare(got[1:], ref[1:], c.name)
+
+
+def _logical_case(L, seed):
+    """Logical K/V rows [L, 4, 256] (bf16 bits), a query and a new token."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    K = W.normal_bf16(rng, (L, 4, 256))
+    V = W.normal_bf16(rng, (L, 4, 256))
+    q = W.normal_bf16(rng, (1, 24, 256))
+    k_new = W.normal_bf16(rng, (1, 4, 256))
+    v_new = W.normal_bf16(rng, (1, 4, 256))
+    return K, V, q, k_new, v_new
+
+
+def _paged(K, V, B, seed):
+    """Lay logical rows out in pages of B rows, in a random physical order
+    (pool of ceil(1.25 n) + 1 pages, the rest NaN); returns caches and the
+    block-table row (one entry more than the rows need, for an appended row)."""
+    L = K.shape[0]
+    n = -(-(L + 1) // B)
+    P = -(-5 * n // 4) + 1
+    rng = np.random.Generator(np.random.PCG64(seed))
+    perm = rng.permutation(P)[:n].astype(np.int32)
+    kc = np.full((P, B, 4, 256), W.BF16_QNAN, np.uint16)
+    vc = np.full((P, B, 4, 256), W.BF16_QNAN, np.uint16)
+    for p in range(n):
+        r = min(B, L - p * B)
+        if r > 0:
+            kc[perm[p], :r] = K[p * B:p * B + r]
+            vc[perm[p], :r] = V[p * B:p * B + r]
+    return kc, vc, perm[None, :]
+
+
+@pytest.mark.parametrize("append", [False, True])
+def test_page_size_bitwise_invariance(append):
+    """The same logical K/V under pages of 784, 832 and 1024 tokens gives the
+    same output bits (page-alignment post §9: page832 and page784 results can
+    be bitwise identical).  Each of these page sizes is a whole number of the
+    decode's 16-token steps (49, 52, 64), so the flattened step list, and with
+    it every workgroup's keys and summation order, is the same.  32K decode,
+    and the 8K appending decode (8192 cached keys + 1 written)."""
+    pa = _pa()
+    L = 8192 if append else 32768
+    K, V, q, k_new, v_new = _logical_case(L, 31 + append)
+    outs = {}
+    for B in (784, 832, 1024):
+        kc, vc, bt = _paged(K, V, B, 100 + B)
+        k, v = to_dev(kc), to_dev(vc)
+        n = L + 1 if append else L
+        lens = np.array([n], np.int32)
+        log(f"page-size invariance B={B} keys={n} append={append}")
+        if append:
+            out = pa.decode_append(to_dev(q), k, v, to_dev(bt), to_dev(lens), n, W.SCALE,
+                                   to_dev(k_new), to_dev(v_new))
+        else:
+            out = pa.decode(to_dev(q), k, v, to_dev(bt), to_dev(lens), n, W.SCALE)
+        _sync()
+        outs[B] = bits(out)
+        if append:
+            # the appended row landed at logical position L
+            kk = bits(k)
+            assert np.array_equal(kk[bt[0, L // B], L % B], k_new[0])
+    assert np.array_equal(outs[784], outs[832]), "784 vs 832 differ"
+    assert np.array_equal(outs[1024], outs[832]), "1024 vs 832 differ"
+    Kf = np.concatenate([K, k_new]) if append else K
+    Vf = np.concatenate([V, v_new]) if append else V
+    kc, vc, bt = _paged(Kf, Vf, 832, 7)
+    ref = oracle.decode(q, kc, vc, bt, np.array([Kf.shape[0]], np.int32), 832, W.SCALE)
+    compare(outs[832], ref, f"page-size invariance append={append}")

@@ -2,7 +2,10 @@
 oracle's fixed fp32 order, bit for bit, in both output types: small ragged
 shapes (one row, a K that leaves lanes without a chunk, K above one register
 pass, a row stride above K, K = 0), the three weight shapes of the
-measurement post at full size, and repeat launches."""
+measurement post at full size, and repeat launches.  Every case is also
+checked directly against the float64 definition: the fp32 output lies
+within the standard fp32 summation error bound of the exact sum, and the
+bf16 output within that bound plus half a bf16 unit in the last place."""
 import numpy as np
 import pytest
 
@@ -42,7 +45,26 @@ def _check(W_bits, x_bits, ldw=None, seed_name=""):
     nb = int(np.sum(got_b != want_b))
     log(f"  mismatches: f32 {nf}, bf16 {nb}")
     assert nf == 0 and nb == 0
+    _check_against_definition(W_bits, x_bits, got_f, got_b)
     return Wd, xd, yb
+
+
+def _check_against_definition(W_bits, x_bits, got_f, got_b):
+    """|y - y_exact| within the fp32 error bound of this summation order (fp32
+    output), plus half a bf16 ulp of the result (bf16 output), per row."""
+    exact = oracle.gemv_f64(W_bits, x_bits)
+    bound = oracle.fp32_sum_error_bound(W_bits, x_bits)
+    err_f = np.abs(got_f.astype(np.float64) - exact)
+    assert np.all(err_f <= bound), f"fp32 output outside the error bound: worst excess {float(np.max(err_f - bound))}"
+    yb = oracle.bf16_bits_to_f64(got_b)
+    # half a bf16 ulp of |y|: 2^(floor(log2|y|) - 8); subnormal quantum 2^-133
+    mag = np.maximum(np.abs(yb), 2.0 ** -126)
+    half_ulp = 2.0 ** (np.floor(np.log2(mag)) - 8)
+    err_b = np.abs(yb - exact)
+    assert np.all(err_b <= bound + half_ulp * (1 + 2.0 ** -8)), "bf16 output outside bound + half ulp"
+    rel = float(np.max(err_f / np.maximum(bound, 1e-300))) if bound.size else 0.0
+    log(f"  vs float64 definition: max |err| fp32 {float(err_f.max()) if err_f.size else 0:.3e}, "
+        f"largest fraction of the bound {rel:.3f}")
 
 
 SMALL = [(1, 8), (7, 520), (9, 5120), (13, 1032), (5, 8192), (3, 16392), (64, 64), (33, 4096)]
