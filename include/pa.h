@@ -72,6 +72,7 @@ extern "C" {
 #define PA_ERR_ALIGN -8         /* a bf16 tensor is not 16-byte aligned */
 #define PA_ERR_LAUNCH -9        /* the HIP runtime rejected a kernel launch */
 #define PA_ERR_SCALE -10        /* scale is not a positive finite number */
+#define PA_ERR_SCRATCH -11      /* pa_decode_noalloc: batch too large for the static scratch */
 
 /*
  * Slot mapping ([PREP] §3.2 and §5): for each token i,
@@ -164,6 +165,30 @@ int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
               int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
               int32_t num_kv_heads, int32_t head_dim, void* workspace,
               size_t workspace_bytes, void* stream);
+
+/*
+ * pa_decode without a workspace argument and without any allocation, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops or harnesses that forbid hipMalloc).  Same arguments,
+ * semantics, kernels and output bits as pa_decode; the split-K partials and
+ * merge metadata go to a file-scope device buffer of the library, 16 MiB per
+ * GPU (held by every GPU the library runs on until the process ends; its
+ * address is looked up once per device on the first call there, with that
+ * device current).  The call runs on the CURRENT device; `stream` must
+ * belong to it.  Calls no hipMalloc / hipFree.
+ * Limit: batches whose pa_decode_workspace_size exceeds 16 MiB return
+ * PA_ERR_SCRATCH (about 1300 sequences at 4 KV heads; fewer with more KV
+ * heads).  Every call on one GPU shares the buffer: two calls that overlap
+ * in time on one GPU (different streams, or different threads) race and
+ * give wrong results; calls queued on one stream are fine.  Nothing in the
+ * buffer needs to start at zero.
+ * Errors: those of pa_decode except PA_ERR_WORKSPACE, plus PA_ERR_SCRATCH.
+ */
+int pa_decode_noalloc(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                      const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
+                      int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, void* stream);
 
 /*
  * One decode step with the new token's KV write in the same launch: for

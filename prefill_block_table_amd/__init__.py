@@ -11,7 +11,8 @@ imports without it.
 """
 import importlib
 
-_API = ("LIB_PATH", "PAError", "build_info", "decode", "decode_append", "decode_workspace",
+_API = ("LIB_PATH", "PAError", "build_info", "decode", "decode_append", "decode_noalloc",
+        "decode_workspace",
         "page_size_for_hybrid", "decode_input_prep", "prefill_workspace", "prefill_workspace_size",
         "prefill_varlen", "gemv",
         "decode_workspace_size", "kv_write", "kv_write_fused", "lib", "prefill_chunk",

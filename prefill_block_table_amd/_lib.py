@@ -24,6 +24,8 @@ lib.pa_kv_write_fused.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _i32, _vp, _
 lib.pa_decode_workspace_size.argtypes = [_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 lib.pa_decode.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
                           _i32, _i32, _i32, _vp, _sz, _vp]
+lib.pa_decode_noalloc.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32, _f32,
+                                  _i32, _i32, _i32, _vp]
 lib.pa_decode_append.argtypes = [_vp, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _i32, _i32, _i32,
                                  _f32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]
 lib.pa_prefill_chunk.argtypes = [_vp, _vp, _i32, _i32, _i32, _vp, _vp, _i64, _vp, _i32, _i32,
@@ -33,7 +35,7 @@ lib.pa_prefill_varlen.argtypes = [_vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _i
 lib.pa_prefill_varlen.restype = ctypes.c_int
 lib.pa_prefill_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]
 for _f in ("pa_slot_mapping", "pa_kv_write", "pa_kv_write_fused", "pa_decode_workspace_size",
-           "pa_decode", "pa_decode_append", "pa_prefill_chunk", "pa_prefill_workspace_size"):
+           "pa_decode", "pa_decode_noalloc", "pa_decode_append", "pa_prefill_chunk", "pa_prefill_workspace_size"):
     getattr(lib, _f).restype = ctypes.c_int
 lib.pa_decode_input_prep.argtypes = [_vp, _i64, _vp, _vp, _i32, _i64, _i64, _vp, _i32, _vp, _i32,
                                      _vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp]
@@ -281,6 +283,30 @@ def decode(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale: 
                          bt.shape[1], _ptr(seq_lens), S, int(max_seq_len), B, float(scale),
                          GQA * H, H, HEAD_DIM, _ptr(workspace), workspace.numel(), _stream(q)),
            "pa_decode")
+    return out
+
+
+def decode_noalloc(q, k_cache, v_cache, block_table, seq_lens, max_seq_len: int, scale: float,
+                   out: torch.Tensor) -> torch.Tensor:
+    """decode() with no workspace and no allocation (pa_decode_noalloc): the
+    library's own per-GPU scratch buffer holds the partials.  `out` must be
+    given (this call allocates nothing)."""
+    P, B, H, stride = _cache_geometry(k_cache, v_cache)
+    _need(q, "q", _BF16, k_cache.device)
+    _need(block_table, "block_table", (torch.int32,), k_cache.device)
+    _need(seq_lens, "seq_lens", (torch.int32,), k_cache.device)
+    _need(out, "out", _BF16, k_cache.device)
+    S = q.shape[0]
+    if q.shape != (S, GQA * H, HEAD_DIM) or out.shape != q.shape:
+        raise ValueError("q and out must be [num_seqs, 6 * num_kv_heads, 256]")
+    bt = block_table if block_table.dim() == 2 else block_table.view(1, -1)
+    if bt.shape[0] < S or seq_lens.numel() < S:
+        raise ValueError("block_table / seq_lens have fewer rows than q")
+    if torch.cuda.current_device() != q.device.index:
+        raise ValueError("pa_decode_noalloc runs on the current device; q is on another one")
+    _check(lib.pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), stride, _ptr(bt),
+                                 bt.shape[1], _ptr(seq_lens), S, int(max_seq_len), B, float(scale),
+                                 GQA * H, H, HEAD_DIM, _stream(q)), "pa_decode_noalloc")
     return out
 
 

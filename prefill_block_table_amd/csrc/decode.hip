@@ -50,6 +50,8 @@
 // rows never reach the output.
 #include <math.h>
 
+#include <mutex>
+
 #include "pa_device.h"
 #include "pa_internal.h"
 
@@ -885,6 +887,37 @@ int64_t live_steps_host(int64_t L, int32_t B, int32_t spp, int32_t step_tokens) 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 }  // namespace
+
+// Workspace of pa_decode_noalloc, for callers that cannot allocate (code
+// under HIP graph capture, serving loops that forbid hipMalloc).  In host
+// code `scratch` names a host-side stand-in, not the device buffer: kernels
+// only ever receive the address hipGetSymbolAddress returns for it.  Every
+// call on one GPU shares the buffer; nothing in it needs to start at zero
+// (each launch writes what it later reads).
+static __device__ __align__(256) char scratch[kDecodeScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t decode_scratch_for_current_device(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidValue;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
+}
 
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
                        int32_t num_kv_heads) {

@@ -127,7 +127,8 @@ static int decode_common(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          const int32_t* seq_lens, int32_t num_seqs, int32_t max_seq_len,
                          int32_t block_size, float scale, int32_t num_q_heads,
                          int32_t num_kv_heads, int32_t head_dim, void* workspace,
-                         size_t workspace_bytes, const pa::DecodeAppend* append, void* stream) {
+                         size_t workspace_bytes, const pa::DecodeAppend* append, void* stream,
+                         bool validate_only = false) {
   if (!out || !q || !block_table || !seq_lens) return PA_ERR_NULL;
   if (!scale_ok(scale)) return PA_ERR_SCALE;
   int rc = check_cache(k_cache, v_cache, page_stride, block_size, num_kv_heads);
@@ -141,6 +142,7 @@ static int decode_common(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
   if (!aligned16(out) || !aligned16(q)) return PA_ERR_ALIGN;
   const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads);
   if (plan.steps_ub >= pa::kMaxDecodeSteps) return PA_ERR_SIZE;
+  if (validate_only) return PA_OK;
   if (!workspace || workspace_bytes < plan.bytes) return PA_ERR_WORKSPACE;
   if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return PA_ERR_ALIGN;
   return launch_status(pa::launch_decode(out, q, k_cache, v_cache, page_stride, block_table,
@@ -158,6 +160,31 @@ int pa_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
   return decode_common(out, q, k_cache, v_cache, page_stride, block_table, bt_stride, seq_lens,
                        num_seqs, max_seq_len, block_size, scale, num_q_heads, num_kv_heads,
                        head_dim, workspace, workspace_bytes, nullptr, stream);
+}
+
+int pa_decode_noalloc(uint16_t* out, const uint16_t* q, const uint16_t* k_cache,
+                      const uint16_t* v_cache, int64_t page_stride, const int32_t* block_table,
+                      int32_t bt_stride, const int32_t* seq_lens, int32_t num_seqs,
+                      int32_t max_seq_len, int32_t block_size, float scale, int32_t num_q_heads,
+                      int32_t num_kv_heads, int32_t head_dim, void* stream) {
+  // Size check first (host arithmetic only), then the per-device buffer.
+  if (block_size >= 1 && num_kv_heads >= 1 && num_kv_heads <= 64 && num_seqs >= 1 &&
+      num_seqs <= 65535 && max_seq_len >= 1 && (int64_t)max_seq_len + block_size <= INT32_MAX) {
+    const pa::DecodePlan plan = pa::plan_decode(num_seqs, max_seq_len, block_size, num_kv_heads);
+    if (plan.bytes > pa::kDecodeScratchBytes) return PA_ERR_SCRATCH;
+  }
+  void* ws = nullptr;
+  size_t ws_bytes = 0;
+  // Argument errors are reported before the device is touched.
+  int rc = decode_common(out, q, k_cache, v_cache, page_stride, block_table, bt_stride, seq_lens,
+                         num_seqs, max_seq_len, block_size, scale, num_q_heads, num_kv_heads,
+                         head_dim, nullptr, 0, nullptr, nullptr, /*validate_only=*/true);
+  if (rc) return rc;
+  if (pa::decode_scratch_for_current_device(&ws) != hipSuccess) return PA_ERR_LAUNCH;
+  ws_bytes = pa::kDecodeScratchBytes;
+  return decode_common(out, q, k_cache, v_cache, page_stride, block_table, bt_stride, seq_lens,
+                       num_seqs, max_seq_len, block_size, scale, num_q_heads, num_kv_heads,
+                       head_dim, ws, ws_bytes, nullptr, stream);
 }
 
 int pa_decode_append(uint16_t* out, const uint16_t* q, uint16_t* k_cache, uint16_t* v_cache,
@@ -326,6 +353,7 @@ const char* pa_strerror(int code) {
     case PA_ERR_ALIGN: return "a tensor is not aligned (bf16 tensors: 16 bytes, workspace: 256 bytes)";
     case PA_ERR_SCALE: return "scale must be a positive finite number";
     case PA_ERR_LAUNCH: return "the HIP runtime rejected a kernel launch";
+    case PA_ERR_SCRATCH: return "the batch needs more decode scratch than the library's static buffer holds (16 MiB): use pa_decode with a workspace";
     default: return "unknown error code";
   }
 }

@@ -61,6 +61,13 @@ hipError_t launch_decode(uint16_t* out, const uint16_t* q, const uint16_t* k_cac
                          const DecodePlan& plan, void* workspace, const DecodeAppend* append,
                          hipStream_t stream);
 
+// Allocation-free decode (pa_decode_noalloc): the same kernels with the
+// workspace in a file-scope device buffer of kDecodeScratchBytes (one copy
+// per GPU, alive until the process ends).  Its device address is looked up
+// once per device (hipGetSymbolAddress with that device current) and kept.
+constexpr size_t kDecodeScratchBytes = (size_t)16 << 20;
+hipError_t decode_scratch_for_current_device(void** ptr);
+
 // Chunked prefill work plan: how many items (query head x 128-row tile) run
 // whole, and how the rest are cut along their key groups.
 constexpr int kPrefillSlots = 256;      // workgroups per round: one per MI355X CU

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
                           "pa_decode_workspace_size", "pa_decode", "pa_decode_append",
                           "pa_prefill_chunk", "pa_prefill_workspace_size", "pa_prefill_varlen",
                           "pa_page_size_for_hybrid", "pa_decode_input_prep",
-                          "pa_gemv_bf16", "pa_strerror", "pa_build_info"}
+                          "pa_gemv_bf16", "pa_strerror", "pa_build_info", "pa_decode_noalloc"}
     out = subprocess.run(["nm", "-D", "--defined-only", pa.LIB_PATH], capture_output=True,
                          text=True).stdout
     exported = set(re.findall(r" T (pa_\w+)", out))
@@ -256,3 +256,23 @@ def test_pages_of_4gib_rejected():
     # one below the limit passes the page-size check (and fails on a later one)
     assert _decode(B=big4 - 1, page_stride=big4 * 1024, bt_stride=1, max_seq_len=100,
                    ws=None) == C["PA_ERR_WORKSPACE"]
+
+
+def test_decode_noalloc_rejects_batches_beyond_its_scratch():
+    """The allocation-free decode checks the batch against its static 16 MiB
+    buffer on the host, before any device call, and validates arguments as
+    pa_decode does (its workspace argument aside)."""
+    def call(**kw):
+        a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, ps=64 * 1024, bt=FAKE, bts=16, sl=FAKE, S=4000,
+                 L=1000, B=64, scale=0.0625, hq=24, hkv=4, d=256)
+        a.update(kw)
+        return pa.lib.pa_decode_noalloc(a["out"], a["q"], a["k"], a["v"], a["ps"], a["bt"], a["bts"],
+                                        a["sl"], a["S"], a["L"], a["B"], a["scale"], a["hq"], a["hkv"],
+                                        a["d"], None)
+    assert pa.decode_workspace_size(4000, 1000, 64, 4) > (16 << 20)
+    assert call() == C["PA_ERR_SCRATCH"]
+    assert "scratch" in pa.strerror(C["PA_ERR_SCRATCH"])
+    assert call(S=1, out=None) == C["PA_ERR_NULL"]
+    assert call(S=1, d=128) == C["PA_ERR_UNSUPPORTED"]
+    assert call(S=1, bts=15) == C["PA_ERR_TABLE"]           # 15 * 64 < 1000
+    assert call(S=1, scale=-1.0) == C["PA_ERR_SCALE"]
