@@ -12,9 +12,13 @@
 // the end.  Each K or V operand read from LDS so feeds two MFMAs (two 16-row
 // blocks), half the LDS traffic per flop of a 16-row wave.  Waves w and
 // w + 4 share a SIMD; waves 4..7 run each group's PV one iteration late, so
-// on every SIMD one wave's soft-max meets the other wave's MFMAs.  Keys stream through LDS one 64-token group
-// of one page at a time (the page's tail group is masked when the page size
-// is not a multiple of 64).  Per group and wave, for row blocks rb = 0, 1:
+// on every SIMD one wave's soft-max meets the other wave's MFMAs.  Keys
+// stream through LDS in groups of 64 consecutive logical tokens, gathered
+// through the block table row by row: a group lies in one page or, when the
+// page size is not a multiple of 64 ([ALIGN] §2: 784 = 12 x 64 + 16), spans
+// two, so only the context's last group is short (the pages' kernels mask a
+// tail group in every such page instead; pages under 64 tokens make groups
+// of one page).  Per group and wave, for row blocks rb = 0, 1:
 //   S^T[32 keys x 16 rows] = K[32 x 256] Q_rb^T    (16 MFMA 16x16x32)
 //   online softmax on S^T: each lane holds 8 scores of one query row, so
 //   the row max and sum take two cross-lane swaps; the accumulator is
@@ -29,7 +33,7 @@
 // come out of LDS with the gfx950 transposing read.  Groups entirely above
 // the causal diagonal of the tile are never visited, a wave skips a key half
 // that lies wholly above its rows, and the mask is evaluated only on groups
-// that cross the diagonal or end a page early.
+// that cross the diagonal or end the context.
 #include <math.h>
 
 #include <algorithm>
@@ -41,7 +45,7 @@
 namespace pa {
 
 const char* const kPrefillVariant =
-    "prefill-v10(bm128,8waves,pairs-32rows-keyhalves,adjacent-pairs,lean-softmax,bn64,mfma16x16x32,st-orient,lds-dma-kv,2k3v-tiles,"
+    "prefill-v11(bm128,8waves,pairs-32rows-keyhalves,adjacent-pairs,lean-softmax,bn64-logical-groups-span-pages,mfma16x16x32,st-orient,lds-dma-kv,2k3v-tiles,"
     "late-pv-on-waves4-7,"
     "tr16-vt,lazy-rescale,heavy-first,xcd-kvhead-map,hw-bf16-pack)";
 
@@ -281,9 +285,13 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int kv_len = start_pos + q_len;
   const int tile_last = min(q0 + kBM, q_len) - 1;
   const int kv_end = a.causal ? start_pos + tile_last + 1 : kv_len;
-  const int upp = (B + kGroup - 1) / kGroup;
-  const int last_page = (kv_end - 1) / B;
-  const int units = last_page * upp + (kv_end - last_page * B + kGroup - 1) / kGroup;
+  // Key groups are runs of GK = min(B, 64) consecutive logical keys: group u
+  // holds keys GK*u .. GK*u + GK - 1 (the last one cut at kv_end).  With
+  // pages of 64 tokens or more a group lies in one page or spans two (a page
+  // of 784 = 12 x 64 + 16 tokens hands its last 16 rows and the next page's
+  // first 48 to one group), so no group is a masked page tail.
+  const int GK = B < kGroup ? B : kGroup;
+  const int units = (kv_end + GK - 1) / GK;
   // this workgroup's key groups [ga, gb) of the tile
   const int ga = part < 0 ? 0 : (int)((int64_t)units * part / a.split);
   const int gb = part < 0 ? units : (int)((int64_t)units * (part + 1) / a.split);
@@ -314,25 +322,40 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   // (All per-lane values here are derived from a fresh lane index inside
   // issue() so that none is held in a register across the loop.)
 
-  // Issue cursor: logical page ip, group ig inside it; the block-table entry
-  // is read (a scalar load) when the first group of a new page is issued.
-  int ip = ga / upp, ig = ga % upp, ip_loaded = -1;
-  int64_t ip_base = 0;
+  // Issue cursor: group iu.  The block-table entries of the (at most two)
+  // pages a group touches are scalar loads, kept for the next group (whose
+  // first page is this group's last).
+  int iu = ga;
+  int pa_idx = -1, pb_idx = -1;
+  int64_t pa_base = 0, pb_base = 0;
   // This wave's share of the next group: rows 8w .. 8w+7 of K (into K tile
   // kst) and of V (into V tile vst), four direct-to-LDS loads each (rows
-  // 8w + 2j on lanes 0..31, 8w + 2j + 1 on lanes 32..63).  Rows past the group's live end reload the page's first
-  // row (finite; masked out of the softmax).
+  // 8w + 2j on lanes 0..31, 8w + 2j + 1 on lanes 32..63).  Rows past the
+  // group's live end reload its first row (finite; masked out of the softmax).
   auto issue = [&](char* kst, char* vst) {
-    if (ip != ip_loaded) {
-      ip_loaded = ip;
-      ip_base = (int64_t)load_const_i32(bt + ip) * page_bytes;
+    const int key0 = iu * GK;
+    const int live = min(GK, kv_end - key0);
+    const int pg = key0 / B;                       // first page of the group
+    const int off = key0 - pg * B;                 // its first row there
+    const int na = min(live, B - off);             // rows in that page; the rest in page pg + 1
+    if (pg != pa_idx) {
+      if (pg == pb_idx) {
+        pa_base = pb_base;
+      } else {
+        pa_base = (int64_t)load_const_i32(bt + pg) * page_bytes;
+      }
+      pa_idx = pg;
     }
-    const int live = min(kGroup, min(B - ig * kGroup, kv_end - (ip * B + ig * kGroup)));
-    const uint32_t gofs = (uint32_t)(ig * kGroup) * rs_bytes;
-    const char* kp = kbase_g + ip_base;
-    const char* vp = vbase_g + ip_base;
+    if (na < live && pb_idx != pg + 1) {
+      pb_base = (int64_t)load_const_i32(bt + pg + 1) * page_bytes;
+      pb_idx = pg + 1;
+    }
+    ++iu;
+    const uint32_t gofs = (uint32_t)off * rs_bytes;
+    const char* kp = kbase_g + pa_base;
+    const char* vp = vbase_g + pa_base;
     const int ln = lane_here(), pos = ln & 31, half = ln >> 5;
-    if (live == kGroup) {
+    if (na == kGroup) {
       const uint32_t k_src = (uint32_t)half * rs_bytes + ((uint32_t)(pos ^ (8 * (w & 1) + half)) << 4);
       const uint32_t v_src = (uint32_t)half * rs_bytes + ((uint32_t)(pos ^ (2 * half)) << 4);
       // whole group: every row is live; row offsets are scalar
@@ -344,18 +367,23 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         __builtin_amdgcn_global_load_lds(vp + rowofs + (v_src ^ (64u * j)), (PA_LDS void*)(vst + ro), 16, 0, 0);
       }
     } else {
+      // a short group (the context's last, or one of a page smaller than
+      // 64), or one that continues in the next page
+      const int64_t db = pb_base - pa_base;        // second page, relative to the first
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int row = 8 * w + 2 * j + half;
-        const uint32_t rb = row < live ? gofs + (uint32_t)row * rs_bytes : 0u;
+        const bool in_b = row >= na && row < live;
+        const uint32_t rb = row < na ? gofs + (uint32_t)row * rs_bytes
+                                     : (in_b ? (uint32_t)(row - na) * rs_bytes : gofs);
+        const int64_t pbase = in_b ? db : 0;
         const int ro = (8 * w + 2 * j) * kRowBytes;
-        __builtin_amdgcn_global_load_lds(kp + (rb + ((uint32_t)(pos ^ kswz(row)) << 4)),
+        __builtin_amdgcn_global_load_lds(kp + pbase + (rb + ((uint32_t)(pos ^ kswz(row)) << 4)),
                                          (PA_LDS void*)(kst + ro), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + (rb + ((uint32_t)(pos ^ vswz(row)) << 4)),
+        __builtin_amdgcn_global_load_lds(vp + pbase + (rb + ((uint32_t)(pos ^ vswz(row)) << 4)),
                                          (PA_LDS void*)(vst + ro), 16, 0, 0);
       }
     }
-    if (++ig == upp) { ig = 0; ++ip; }
   };
 
   // Per-lane operand read offsets within a K or V tile (this wave's key half
@@ -433,7 +461,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     }
   };
 
-  int cp = ga / upp, cg = ga % upp;        // compute cursor (page, group)
+  int cu = ga;                              // compute cursor (group)
   // One barrier per group.  Waves w and w + 4 share a SIMD.  Waves 0..3 run
   // each group as scores, softmax, PV; waves 4..7 run the PV of a group at
   // the start of the next iteration, before that one's scores, so on every
@@ -454,9 +482,9 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     const bool more = u + 1 < gb;
 
     auto qksm = [&]() {
-      const int key0 = cp * B + cg * kGroup;
-      const int n = min(kGroup, min(B - cg * kGroup, kv_end - key0));
-      if (++cg == upp) { cg = 0; ++cp; }
+      const int key0 = cu * GK;
+      const int n = min(GK, kv_end - key0);
+      ++cu;
       const int hk0 = key0 + kHalfKeys * kh;   // first key of this wave's half
       // The half holds no live key, or (causal) every key of it lies after
       // the wave's last row: nothing to add.
@@ -694,9 +722,8 @@ __global__ void __launch_bounds__(256) prefill_merge_kernel(PrefillArgs a) {
 int tile_units(int32_t q_len, int32_t start_pos, int32_t causal, int32_t block_size, int tile) {
   const int64_t kv_end = causal ? (int64_t)start_pos + std::min<int64_t>((int64_t)(tile + 1) * kBM, q_len)
                                 : (int64_t)start_pos + q_len;
-  const int64_t upp = (block_size + kGroup - 1) / kGroup;
-  const int64_t last_page = (kv_end - 1) / block_size;
-  return (int)(last_page * upp + (kv_end - last_page * block_size + kGroup - 1) / kGroup);
+  const int64_t gk = block_size < kGroup ? block_size : kGroup;   // keys per group
+  return (int)((kv_end + gk - 1) / gk);
 }
 
 }  // namespace
