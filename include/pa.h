@@ -36,8 +36,11 @@
  *    PA_ERR_UNSUPPORTED.  Any block_size >= 1 works as long as one page of
  *    one cache, block_size * num_kv_heads * 256 * 2 bytes, stays below
  *    4 GiB (kernels address rows inside a page with 32-bit byte offsets;
- *    larger pages return PA_ERR_BLOCK_SIZE); pages whose size is not a
- *    multiple of 64 cost one masked tail group per page.
+ *    larger pages return PA_ERR_BLOCK_SIZE).  Prefill gathers keys in
+ *    64-token logical groups that may span two pages, so a page size that
+ *    is not a multiple of 64 costs no masked tail group per page; decode
+ *    walks 16-token steps inside pages (784, 832 and 1024 are whole numbers
+ *    of them).
  *  - Ownership: the caller owns every buffer, including the decode
  *    workspace.  The library never allocates or frees device memory and
  *    keeps no state between calls.
