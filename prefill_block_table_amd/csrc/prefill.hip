@@ -423,6 +423,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   // (this wave's key half): V^T operands come from transposing LDS reads one
   // batch of two d-blocks ahead of the MFMAs.
   auto pv = [&](const u32x4 (&pbv)[2], const uint32_t vbase) {
+    __builtin_amdgcn_s_setprio(1);
     u32x2 va[2][2][2];
     // batch b: d-blocks 2*b, 2*b + 1
     auto vread = [&](int b, u32x2 (&d)[2][2]) {
@@ -459,6 +460,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
         for (int rb = 0; rb < 2; ++rb) o[2 * b + t][rb] = mfma16(av, pbv[rb], o[2 * b + t][rb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
   };
 
   int cu = ga;                              // compute cursor (group)
@@ -497,6 +499,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) s[kb][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    __builtin_amdgcn_s_setprio(1);
     {
       const uint32_t kbase = lds_addr(kt) + k_lane;
       u32x4 kv[2][2];
@@ -529,6 +532,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
           for (int rb = 0; rb < 2; ++rb) s[kb][rb] = mfma16(kv[cur][kb], qb[rb][ds], s[kb][rb]);
       }
     }
+    __builtin_amdgcn_s_setprio(0);
     // Soft-max.  s[kb][rb][r] is key hk0 + 16*kb + 4*kq + r of query row
     // 16*rb + c16; scores stay unscaled until the exponent (one fma).
     const bool need_mask = (kHalfKeys * kh + kHalfKeys > n) || (a.causal && hk0 + kHalfKeys - 1 > wave_first_pos);
