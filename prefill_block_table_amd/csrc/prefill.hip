@@ -328,6 +328,10 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   int iu = ga;
   int pa_idx = -1, pb_idx = -1;
   int64_t pa_base = 0, pb_base = 0;
+  // Position of group iu: page ipg, row ioff there (advanced by GK per group;
+  // GK <= B, so a step crosses at most one page boundary).
+  int ipg = (ga * GK) / B;
+  int ioff = ga * GK - ipg * B;
   // This wave's share of the next group: rows 8w .. 8w+7 of K (into K tile
   // kst) and of V (into V tile vst), four direct-to-LDS loads each (rows
   // 8w + 2j on lanes 0..31, 8w + 2j + 1 on lanes 32..63).  Rows past the
@@ -335,9 +339,11 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   auto issue = [&](char* kst, char* vst) {
     const int key0 = iu * GK;
     const int live = min(GK, kv_end - key0);
-    const int pg = key0 / B;                       // first page of the group
-    const int off = key0 - pg * B;                 // its first row there
+    const int pg = ipg;                            // first page of the group
+    const int off = ioff;                          // its first row there
     const int na = min(live, B - off);             // rows in that page; the rest in page pg + 1
+    ioff += GK;
+    if (ioff >= B) { ioff -= B; ++ipg; }
     if (pg != pa_idx) {
       if (pg == pb_idx) {
         pa_base = pb_base;
