@@ -46,7 +46,7 @@ namespace pa {
 
 const char* const kPrefillVariant =
     "prefill-v11(bm128,8waves,pairs-32rows-keyhalves,adjacent-pairs,lean-softmax,bn64-logical-groups-span-pages,mfma16x16x32,st-orient,lds-dma-kv,2k3v-tiles,"
-    "late-pv-on-waves4-7,"
+    "late-pv-on-waves4-7,prio-mfma-phases,"
     "tr16-vt,lazy-rescale,heavy-first,xcd-kvhead-map,hw-bf16-pack)";
 
 namespace {
