@@ -281,8 +281,14 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
  * max_seqlen_q, max_seqlen_k   host bounds of the device lengths (lengths
  *                above them are clamped to them).  A sequence with no rows,
  *                or with fewer keys than rows, is left unwritten.
- * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE,
- * PA_ERR_TABLE, PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
+ * Device offsets are clamped to [0, total_q]; if they decrease somewhere,
+ * which sequences get written is unspecified, but no access leaves q, out or
+ * a sequence's block-table row.  The launch has (total_q / 128 + num_seqs) *
+ * num_q_heads workgroups: its size follows the rows batched, not num_seqs
+ * times the longest sequence.
+ * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE
+ * (also when that workgroup count exceeds 2^31 - 1), PA_ERR_TABLE,
+ * PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
  */
 int pa_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
                       const int32_t* cu_seqlens_q, const int32_t* seqused_k, int32_t num_seqs,

@@ -264,8 +264,7 @@ int pa_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
   if (num_seqs < 1 || total_q < 1 || max_seqlen_q < 1 || max_seqlen_k < 1 ||
       (int64_t)max_seqlen_k + block_size > INT32_MAX)
     return PA_ERR_SIZE;
-  const int64_t grid = (int64_t)num_seqs * num_q_heads * ((max_seqlen_q + 127) / 128);
-  if (grid > INT32_MAX) return PA_ERR_SIZE;
+  if (pa::varlen_grid(total_q, num_seqs, num_kv_heads) > INT32_MAX) return PA_ERR_SIZE;
   if (bt_stride < 1 || (int64_t)bt_stride * block_size < max_seqlen_k) return PA_ERR_TABLE;
   if (!aligned16(out) || !aligned16(q)) return PA_ERR_ALIGN;
   return launch_status(pa::launch_prefill_varlen(out, q, total_q, cu_seqlens_q, seqused_k, num_seqs,

@@ -113,6 +113,13 @@ struct InputPrepArgs {
 
 hipError_t launch_decode_input_prep(const InputPrepArgs& a, hipStream_t stream);
 
+// Workgroups of a several-sequence prefill launch: total_q / 128 + num_seqs
+// tile slots (each sequence's rows and at most one spare slot), each one
+// workgroup per query head (6 per KV head).
+inline int64_t varlen_grid(int32_t total_q, int32_t num_seqs, int32_t num_kv_heads) {
+  return ((int64_t)total_q / 128 + num_seqs) * num_kv_heads * 6;
+}
+
 hipError_t launch_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total_q,
                                  const int32_t* cu_seqlens_q, const int32_t* seqused_k,
                                  int32_t num_seqs, int32_t max_seqlen_q, int32_t max_seqlen_k,

@@ -101,11 +101,15 @@ struct PrefillArgs {
   // Several sequences (pa_prefill_varlen; NULL cu_seqlens_q: one sequence,
   // q_len / start_pos / block_table above): sequence s has query rows
   // cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and seqused_k[s] keys, its block-table
-  // row at block_table + s * bt_stride; num_q_tiles is then the tile count of
-  // the longest sequence, every sequence gets 6 * num_kv_heads * num_q_tiles
-  // workgroups and those past its rows leave at once.
+  // row at block_table + s * bt_stride.  Sequence s owns the tile slots
+  // P(s) .. P(s+1)-1 with P(s) = cu_seqlens_q[s] / 128 + s, which leave room
+  // for its ceil(rows / 128) tiles (at most one slot to spare), and each slot
+  // is 6 * num_kv_heads workgroups; the grid covers total_q / 128 + num_seqs
+  // slots, so its size follows the rows actually batched rather than
+  // num_seqs times the longest sequence.
   const int32_t* cu_seqlens_q;
   const int32_t* seqused_k;
+  int32_t num_seqs;
   int32_t bt_stride;
   int32_t total_q;         // rows of q / out
   int32_t max_q;           // host bounds the device lengths are clamped to
@@ -217,20 +221,42 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int L = blockIdx.x;
   int item = L, part = -1;
   int32_t q_len = a.q_len, start_pos = a.start_pos;
+  int T = a.num_q_tiles;                             // tiles of this workgroup's sequence
   const int32_t* bt = a.block_table;
   int64_t row0 = 0;                                  // first q / out row of the sequence
   if (a.cu_seqlens_q) {
-    const int per_seq = a.num_kv_heads * kGqa * a.num_q_tiles;
-    const int sq = L / per_seq;
-    item = L - sq * per_seq;
-    // device lengths are clamped to the host-checked bounds, so no load
-    // leaves q, out or the sequence's block-table row
-    const int c0 = min(load_const_i32(a.cu_seqlens_q + sq), a.total_q);
-    const int c1 = min(load_const_i32(a.cu_seqlens_q + sq + 1), a.total_q);
+    // Sequence of slot t = L / Hq: the largest s with P(s) <= t, found as the
+    // count of such s in 0 .. num_seqs (P is nondecreasing) with one vector
+    // load per 64 entries and a ballot.  Device offsets are clamped to
+    // [0, total_q] and lengths to the host-checked bounds, so no load leaves
+    // q, out or the sequence's block-table row; offsets that decrease give
+    // slots that match no sequence, and those workgroups leave.
+    const int Hqs = a.num_kv_heads * kGqa;
+    const int t = L / Hqs;
+    const int ln = threadIdx.x & 63;
+    int cnt = 0;
+    for (int base = 0; base <= a.num_seqs; base += 64) {
+      const int i = base + ln;
+      bool le = false;
+      if (i <= a.num_seqs) {
+        const int c = min(max(a.cu_seqlens_q[i], 0), a.total_q);
+        le = c / kBM + i <= t;
+      }
+      cnt += __popcll(__ballot(le));
+    }
+    const int sq = __builtin_amdgcn_readfirstlane(cnt) - 1;
+    if (sq < 0 || sq >= a.num_seqs) return;
+    const int c0 = min(max(load_const_i32(a.cu_seqlens_q + sq), 0), a.total_q);
+    const int c1 = min(max(load_const_i32(a.cu_seqlens_q + sq + 1), 0), a.total_q);
+    const int p0 = c0 / kBM + sq;
+    if (t >= c1 / kBM + sq + 1) return;
     q_len = min(c1 - c0, a.max_q);
     const int kv = min(load_const_i32(a.seqused_k + sq), a.max_k);
     start_pos = kv - q_len;                          // the chunk's rows end at the last key
-    if (c0 < 0 || q_len <= 0 || start_pos < 0) return;
+    if (q_len <= 0 || start_pos < 0) return;
+    T = (q_len + kBM - 1) / kBM;
+    item = L - Hqs * p0;
+    if (item >= Hqs * T) return;                     // the sequence's spare slot
     row0 = c0;
     bt = a.block_table + (int64_t)sq * a.bt_stride;
   } else if (L >= a.num_full) {
@@ -239,8 +265,7 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
     part = qq % a.split;
   }
   int g, head, tile;
-  map_item(item, a.num_kv_heads, a.num_q_tiles, g, head, tile);
-  if (tile * kBM >= q_len) return;                   // past the sequence's rows (several sequences)
+  map_item(item, a.num_kv_heads, T, g, head, tile);
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   // wave index, uniform per wave: LDS destinations and row bases stay scalar
@@ -789,6 +814,7 @@ hipError_t launch_prefill(uint16_t* out, const uint16_t* q, int32_t q_len, int32
   a.split = plan.split;
   a.cu_seqlens_q = nullptr;
   a.seqused_k = nullptr;
+  a.num_seqs = 1;
   a.bt_stride = 0;
   a.total_q = q_len;
   a.max_q = q_len;
@@ -833,11 +859,12 @@ hipError_t launch_prefill_varlen(uint16_t* out, const uint16_t* q, int32_t total
   a.part_ml = nullptr;
   a.cu_seqlens_q = cu_seqlens_q;
   a.seqused_k = seqused_k;
+  a.num_seqs = num_seqs;
   a.bt_stride = bt_stride;
   a.total_q = total_q;
   a.max_q = max_seqlen_q;
   a.max_k = max_seqlen_k;
-  const int64_t grid = (int64_t)num_seqs * num_kv_heads * kGqa * a.num_q_tiles;
+  const int64_t grid = varlen_grid(total_q, num_seqs, num_kv_heads);
   hipLaunchKernelGGL(prefill_kernel, dim3((uint32_t)grid), dim3(kWavesPf * 64), 0, stream, a);
   return hipGetLastError();
 }

@@ -218,6 +218,8 @@ def test_prefill_varlen_validation():
     assert call(scale=-1.0) == C["PA_ERR_SCALE"]
     assert call(hq=32) == C["PA_ERR_UNSUPPORTED"]
     assert call(q=FAKE_MIS) == C["PA_ERR_ALIGN"]
+    # (total_q / 128 + num_seqs) * num_q_heads workgroups above 2^31 - 1
+    assert call(total=2**31 - 1, hq=384, hkv=64, ps=832 * 64 * 256) == C["PA_ERR_SIZE"]
 
 
 def test_gemv_validation():

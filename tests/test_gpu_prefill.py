@@ -203,6 +203,23 @@ def test_varlen_random_shapes(i):
     _check_varlen(c, causal)
 
 
+def test_varlen_many_sequences():
+    """100 sequences in one call (more than one 64-entry pass of the
+    workgroup's sequence search): one long chunk among 99 short ones at random
+    starts, page 64, causal; the grid follows the rows batched (slots
+    total_q / 128 + 100) rather than 100 x the longest sequence's tiles."""
+    rng = np.random.default_rng(4242)
+    seqs = [(1000, 1500)] + [(int(rng.integers(0, 501)), int(rng.integers(1, 41))) for _ in range(99)]
+    order = rng.permutation(len(seqs))
+    seqs = [seqs[j] for j in order]
+    B = 64
+    pages = sum(-(-(s0 + n) // B) for s0, n in seqs)
+    c = W.make_varlen_prefill_case("varlen_100seqs_b64", 4243, seqs, B, pages + 4, causal=True)
+    log(f"{c.name} long sequence at index {int(np.argmax([n for _, n in seqs]))}, total rows "
+        f"{sum(n for _, n in seqs)}")
+    _check_varlen(c, True)
+
+
 def _check_varlen(c, causal):
     pa = _pa()
     B = c.block_size
