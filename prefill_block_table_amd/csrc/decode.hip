@@ -922,11 +922,7 @@ hipError_t decode_scratch_for_current_device(void** ptr) {
 DecodePlan plan_decode(int32_t num_seqs, int32_t max_seq_len, int32_t block_size,
                        int32_t num_kv_heads) {
   DecodePlan p{};
-#ifdef PA_DECODE_HPW
-  p.heads_per_wg = PA_DECODE_HPW;
-#else
   p.heads_per_wg = num_kv_heads % 4 == 0 ? 4 : (num_kv_heads % 2 == 0 ? 2 : 1);
-#endif
   p.step_tokens = 16 * (kWaves / p.heads_per_wg);
   p.steps_per_page = (block_size + p.step_tokens - 1) / p.step_tokens;
   const int64_t items = (int64_t)num_seqs * (num_kv_heads / p.heads_per_wg);
