@@ -42,8 +42,10 @@
  *    walks 16-token steps inside pages (784, 832 and 1024 are whole numbers
  *    of them).
  *  - Ownership: the caller owns every buffer, including the decode
- *    workspace.  The library never allocates or frees device memory and
- *    keeps no state between calls.
+ *    workspace.  The library never allocates or frees device memory.  Its
+ *    only state between calls is the 16 MiB static device buffer of
+ *    pa_decode_noalloc (part of the library's code object, one per GPU) and
+ *    that buffer's address per device, looked up on the first call there.
  *  - Execution: each call validates its arguments on the host, then only
  *    enqueues kernels on `stream` (a hipStream_t; NULL = the null stream) and
  *    returns without synchronizing.  On any error nothing is enqueued.
@@ -139,10 +141,13 @@ int pa_decode_workspace_size(int32_t num_seqs, int32_t max_seq_len, int32_t bloc
                              int32_t num_kv_heads, size_t* bytes_out);
 
 /*
- * Single-token (q = 1) paged GQA decode ([ALIGN] §7: walk the pages of each
- * sequence in order, look up block_table once per page, iterate 64-token
- * groups inside the page, online softmax; no page skipped, causal range not
- * shortened).  For each sequence s and query head h (KV head g = h / 6):
+ * Single-token (q = 1) paged GQA decode ([ALIGN] §7 defines it: every page
+ * of each sequence, one block_table lookup per page, online softmax; no page
+ * skipped, causal range not shortened.  The pages' kernel iterates 64-token
+ * groups inside a page; this one splits each sequence's keys into 16-token
+ * steps inside pages, spread over the GPU's CUs, and merges the per-CU
+ * partial results in a second launch, in a fixed order).  For each sequence
+ * s and query head h (KV head g = h / 6):
  *   out[s][h] = sum_j softmax_j(scale * q[s][h] . K_j) * V_j
  * over the seq_lens[s] keys j = 0 .. seq_lens[s]-1 of sequence s; the query
  * is the token at position seq_lens[s]-1, whose K/V must already be in the
