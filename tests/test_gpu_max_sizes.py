@@ -44,3 +44,16 @@ def test_prefill_16384_rows_sampled():
     ref = oracle.prefill_chunk(ch.q, start, True, rk, rv, c.block_table, B, c.scale, rows=rows)
     compare(got[rows], ref, f"{c.name} ({len(rows)} rows)")
     assert np.all(np.isfinite(oracle.bf16_bits_to_f64(got))), "non-finite rows"
+
+
+def test_decode_4000_short_sequences():
+    """4000 sequences of 1-40 tokens (page 16), with the appended token: far
+    more items than workgroups, most of them whole inside one workgroup."""
+    import test_gpu_decode as TD
+    rng = np.random.default_rng(74)
+    lens = [int(x) for x in rng.integers(1, 41, size=4000)]
+    B = 16
+    c = W.make_decode_case("decode_4000_seqs_b16", 75, lens, B, sum(-(-(n + 1) // B) for n in lens) + 2,
+                           write_new_token=True)
+    log(f"{c.name} total tokens {sum(lens)}")
+    TD._check_append(c)
