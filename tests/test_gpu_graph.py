@@ -4,7 +4,8 @@ between the replays; every replay must give the eager result bit for bit.
 Covers the two-kernel decode with the fused KV write, the prefill chunk with
 its split plan (partials in the workspace, then the merge kernel), the
 several-sequence prefill, the fused slot-mapping KV write (caches restored
-between replays), the single-token input preparation and the GEMV."""
+between replays), the separate slot mapping, KV write and plain decode in one
+graph, the single-token input preparation and the GEMV."""
 import numpy as np
 import pytest
 
@@ -205,3 +206,37 @@ def test_decode_input_prep_graph_replays():
             o.fill_(-7 if o.dtype != torch.uint8 else 3)
 
     _replay_and_check(run, outs, refs, "decode_input_prep", poison=poison)
+
+
+def test_slot_mapping_kv_write_and_decode_graph_replays():
+    """The separate calls in one graph: pa_slot_mapping, pa_kv_write through
+    those slots, then the plain pa_decode (caches restored between replays)."""
+    import torch
+    pa = _pa()
+    c = W.batched_decode()
+    log("slot_mapping + kv_write + decode graph")
+    k, v = to_dev(c.k_cache), to_dev(c.v_cache)
+    k0, v0 = k.clone(), v.clone()
+    bt, sl, q = to_dev(c.block_tables), to_dev(c.seq_lens), to_dev(c.q)
+    pos, seq = to_dev(c.positions), to_dev(c.token_seq)
+    kn, vn = to_dev(c.k_new), to_dev(c.v_new)
+    ws = pa.decode_workspace(q.shape[0], c.max_seq_len, c.block_size)
+    slots = torch.empty(pos.shape[0], dtype=torch.int64, device="cuda")
+    out = torch.empty_like(q)
+
+    def run():
+        pa.slot_mapping(pos, bt, c.block_size, token_seq=seq, out=slots)
+        pa.kv_write(k, v, kn, vn, slots)
+        pa.decode(q, k, v, bt, sl, c.max_seq_len, c.scale, workspace=ws, out=out)
+
+    run()
+    torch.cuda.synchronize()
+    refs = [k.clone(), v.clone(), slots.clone(), out.clone()]
+
+    def poison():
+        k.copy_(k0)
+        v.copy_(v0)
+        slots.fill_(-7)
+        out.view(torch.int16).fill_(-7)
+
+    _replay_and_check(run, [k, v, slots, out], refs, "slot_mapping + kv_write + decode", poison=poison)
