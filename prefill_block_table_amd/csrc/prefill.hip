@@ -101,12 +101,12 @@ struct PrefillArgs {
   // Several sequences (pa_prefill_varlen; NULL cu_seqlens_q: one sequence,
   // q_len / start_pos / block_table above): sequence s has query rows
   // cu_seqlens_q[s] .. cu_seqlens_q[s+1]-1 and seqused_k[s] keys, its block-table
-  // row at block_table + s * bt_stride.  Sequence s owns the tile slots
-  // P(s) .. P(s+1)-1 with P(s) = cu_seqlens_q[s] / 128 + s, which leave room
-  // for its ceil(rows / 128) tiles (at most one slot to spare), and each slot
-  // is 6 * num_kv_heads workgroups; the grid covers total_q / 128 + num_seqs
-  // slots, so its size follows the rows actually batched rather than
-  // num_seqs times the longest sequence.
+  // row at block_table + s * bt_stride.  Each tile slot is 6 * num_kv_heads
+  // workgroups; the grid covers total_q / 128 + num_seqs slots, so its size
+  // follows the rows actually batched rather than num_seqs times the longest
+  // sequence.  Batches of up to 64 sequences give the slots to the sequences
+  // heaviest (most keys) first; larger ones in input order (see the kernel's
+  // prologue).
   const int32_t* cu_seqlens_q;
   const int32_t* seqused_k;
   int32_t num_seqs;
@@ -225,31 +225,64 @@ __global__ void __launch_bounds__(kWavesPf * 64, 1) prefill_kernel(PrefillArgs a
   const int32_t* bt = a.block_table;
   int64_t row0 = 0;                                  // first q / out row of the sequence
   if (a.cu_seqlens_q) {
-    // Sequence of slot t = L / Hq: the largest s with P(s) <= t, found as the
-    // count of such s in 0 .. num_seqs (P is nondecreasing) with one vector
-    // load per 64 entries and a ballot.  Device offsets are clamped to
-    // [0, total_q] and lengths to the host-checked bounds, so no load leaves
-    // q, out or the sequence's block-table row; offsets that decrease give
-    // slots that match no sequence, and those workgroups leave.
+    // Device offsets are clamped to [0, total_q] and lengths to the
+    // host-checked bounds, so no load leaves q, out or a sequence's
+    // block-table row.
     const int Hqs = a.num_kv_heads * kGqa;
-    const int t = L / Hqs;
+    const int t = L / Hqs;                           // this workgroup's tile slot
     const int ln = threadIdx.x & 63;
-    int cnt = 0;
-    for (int base = 0; base <= a.num_seqs; base += 64) {
-      const int i = base + ln;
-      bool le = false;
-      if (i <= a.num_seqs) {
-        const int c = min(max(a.cu_seqlens_q[i], 0), a.total_q);
-        le = c / kBM + i <= t;
+    int sq = -1, p0 = 0;
+    if (a.num_seqs <= 64) {
+      // Up to 64 sequences: the slots go to the sequences in decreasing order
+      // of their key count (the cost of their heaviest tile; ties by index),
+      // each sequence's tiles together and heaviest first, so the last
+      // workgroups dispatched hold the lightest tiles of the batch.  Lane i
+      // takes sequence i; its rank and the slots of the sequences before it
+      // are counted over the other lanes.
+      int tl = 0, key = -1;
+      if (ln < a.num_seqs) {
+        const int c0 = min(max(a.cu_seqlens_q[ln], 0), a.total_q);
+        const int c1 = min(max(a.cu_seqlens_q[ln + 1], 0), a.total_q);
+        const int ql = min(c1 - c0, a.max_q);
+        const int kvl = min(a.seqused_k[ln], a.max_k);
+        if (ql > 0 && kvl - ql >= 0) { tl = (ql + kBM - 1) / kBM; key = kvl; }
       }
-      cnt += __popcll(__ballot(le));
+      int before = 0;                                // slots of the sequences ranked ahead
+      for (int j = 0; j < a.num_seqs; ++j) {
+        const int kj = __builtin_amdgcn_readlane(key, j);
+        const int tj = __builtin_amdgcn_readlane(tl, j);
+        if (kj > key || (kj == key && j < ln)) before += tj;
+      }
+      const uint64_t mine = __ballot(tl > 0 && t >= before && t < before + tl);
+      if (mine == 0) return;                         // past the batch's last tile
+      sq = __builtin_amdgcn_readfirstlane(__builtin_ctzll(mine));
+      p0 = __builtin_amdgcn_readlane(before, sq);
+    } else {
+      // More sequences: input order.  Sequence s owns the slots from
+      // P(s) = cu_seqlens_q[s] / 128 + s; the sequence of slot t is the
+      // largest s with P(s) <= t, found as the count of such s in 0 ..
+      // num_seqs (P is nondecreasing) with one vector load per 64 entries and
+      // a ballot.  Offsets that decrease give slots that match no sequence,
+      // and those workgroups leave.
+      int cnt = 0;
+      for (int base = 0; base <= a.num_seqs; base += 64) {
+        const int i = base + ln;
+        bool le = false;
+        if (i <= a.num_seqs) {
+          const int c = min(max(a.cu_seqlens_q[i], 0), a.total_q);
+          le = c / kBM + i <= t;
+        }
+        cnt += __popcll(__ballot(le));
+      }
+      sq = __builtin_amdgcn_readfirstlane(cnt) - 1;
+      if (sq < 0 || sq >= a.num_seqs) return;
     }
-    const int sq = __builtin_amdgcn_readfirstlane(cnt) - 1;
-    if (sq < 0 || sq >= a.num_seqs) return;
     const int c0 = min(max(load_const_i32(a.cu_seqlens_q + sq), 0), a.total_q);
     const int c1 = min(max(load_const_i32(a.cu_seqlens_q + sq + 1), 0), a.total_q);
-    const int p0 = c0 / kBM + sq;
-    if (t >= c1 / kBM + sq + 1) return;
+    if (a.num_seqs > 64) {
+      p0 = c0 / kBM + sq;
+      if (t >= c1 / kBM + sq + 1) return;
+    }
     q_len = min(c1 - c0, a.max_q);
     const int kv = min(load_const_i32(a.seqused_k + sq), a.max_k);
     start_pos = kv - q_len;                          // the chunk's rows end at the last key
