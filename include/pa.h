@@ -290,7 +290,8 @@ int pa_prefill_chunk(uint16_t* out, const uint16_t* q_chunk, int32_t q_len, int3
  * which sequences get written is unspecified, but no access leaves q, out or
  * a sequence's block-table row.  The launch has (total_q / 128 + num_seqs) *
  * num_q_heads workgroups: its size follows the rows batched, not num_seqs
- * times the longest sequence.
+ * times the longest sequence.  With up to 64 sequences, the sequences with
+ * the most keys run first (the order changes no result).
  * Errors: PA_ERR_NULL, PA_ERR_BLOCK_SIZE, PA_ERR_UNSUPPORTED, PA_ERR_SIZE
  * (also when that workgroup count exceeds 2^31 - 1), PA_ERR_TABLE,
  * PA_ERR_STRIDE, PA_ERR_ALIGN, PA_ERR_SCALE, PA_ERR_LAUNCH.
