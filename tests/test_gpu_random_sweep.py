@@ -16,7 +16,7 @@ pytestmark = pytest.mark.gpu
 
 PAGES = [1, 2, 7, 15, 16, 31, 32, 33, 48, 63, 64, 65, 66, 96, 100, 127, 128, 129, 130, 191, 192,
          200, 255, 256, 257, 500, 783, 784, 785, 832, 1000, 1023, 1024, 1025]
-N_PREFILL, N_VARLEN, N_DECODE = 48, 24, 48
+N_PREFILL, N_VARLEN, N_DECODE = 96, 48, 96
 
 
 def _page(rng):
